@@ -1,0 +1,38 @@
+"""CPU oracle for the paged-KV-cache hot path.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything in this package. The
+product path (``paged_kv_cache_454_amd``) never imports, calls or links it, and
+this package imports nothing from the product path: the two share no code.
+The only module both sides use is the seeded input generator
+``paged_kv_cache_454_amd.inputs``, which holds none of the method's arithmetic.
+
+Everything here is plain NumPy in float64 (integer work in Python ints),
+written from the definitions on these pages:
+
+* "High-Throughput LLM Inference & Training: A Deep Dive into vLLM"
+  (wpnews.pro), Fig. 1 and Fig. 2 captions.
+* "vLLM Architecture, Memory and Benchmarks Deep Dive" (wpnews.pro),
+  sections 1-4.
+* "Optimizing LLM Inference: A Deep Dive into vLLM's PagedAttention and
+  Continuous Batching" (voronkin.com), KV-cache section, equation M_KV.
+* "Inside vLLM: Anatomy of a High-Throughput LLM Inference System"
+  (syntaxis blog), "Garbage Collection & Reuse" and "FlashAttention-2
+  Integration".
+
+Modules:
+
+* ``accounting`` - the KV-size closed form and the reservation counts of the
+  contiguous and paged policies (pinned by the pages' printed numbers).
+* ``allocator``  - a model of the on-demand block allocator with a FIFO free
+  list (pinned by the worked example and the pages' stated invariants).
+* ``attention``  - the slot-mapped cache write, logical reassembly of a paged
+  cache, dense softmax decode attention, split-context partitions and their
+  log-sum-exp merge, and causal chunked prefill (pinned by brute force,
+  closed-form special cases and a library attention routine).
+
+Parity status: every function above has at least one pin that does not reuse
+its own formula; none is "parity unpinned".
+"""
+
+from . import accounting, allocator, attention  # noqa: F401

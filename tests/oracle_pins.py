@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes the oracle modules it checks as arguments (so a
+deliberately broken copy can be passed in by the mutation tests) and raises
+AssertionError when the oracle disagrees with:
+
+* numbers the pages print (golden fixtures under tests/golden/, each cited),
+* closed forms and invariants the pages state,
+* a pure-Python brute force that walks the physical blocks in logical order
+  (forward mapping block j, offset o -> position j*bs + o; no NumPy),
+* a library attention routine (torch scaled_dot_product_attention in float64
+  on the CPU, with its own grouped-query head mapping), and
+* mathematical special cases (one token, constant values, zero query, ...).
+"""
+
+import json
+import math
+import os
+import random
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- helpers
+
+def _tiny_case(rng, num_seqs, max_len, hq, hkv, d, bs, pool_extra=2, zero_len=False):
+    """Random tiny paged case built without the oracle: dense per-sequence K/V,
+    scattered into a pool by walking blocks forward. Returns the pool, tables,
+    lens and the dense tensors for brute force / library checks."""
+    lens = [rng.randint(1, max_len) for _ in range(num_seqs)]
+    if zero_len:
+        lens[0] = 0
+    nblk = [(t + bs - 1) // bs for t in lens]
+    num_blocks = sum(nblk) + pool_extra
+    ids = list(range(num_blocks))
+    rng.shuffle(ids)
+    kc = np.full((num_blocks, hkv, bs, d), np.nan)
+    vc = np.full((num_blocks, hkv, bs, d), np.nan)
+    tables = np.full((num_seqs, max(1, max(nblk))), -1, dtype=np.int64)
+    dense_k, dense_v = [], []
+    nxt = 0
+    for s in range(num_seqs):
+        K = [[[rng.gauss(0, 1) for _ in range(d)] for _ in range(hkv)] for _ in range(lens[s])]
+        V = [[[rng.gauss(0, 1) for _ in range(d)] for _ in range(hkv)] for _ in range(lens[s])]
+        dense_k.append(K)
+        dense_v.append(V)
+        for j in range(nblk[s]):
+            phys = ids[nxt]
+            nxt += 1
+            tables[s, j] = phys
+            for o in range(bs):
+                pos = j * bs + o
+                if pos < lens[s]:
+                    kc[phys, :, o, :] = K[pos]
+                    vc[phys, :, o, :] = V[pos]
+    q = [[[rng.gauss(0, 1) for _ in range(d)] for _ in range(hq)] for _ in range(num_seqs)]
+    return dict(kc=kc, vc=vc, tables=tables, lens=lens, q=np.array(q), K=dense_k, V=dense_v,
+                bs=bs, hq=hq, hkv=hkv, d=d)
+
+
+def _brute_attend(q, keys, vals, scale):
+    logits = [scale * sum(a * b for a, b in zip(q, k)) for k in keys]
+    top = max(logits)
+    e = [math.exp(z - top) for z in logits]
+    tot = sum(e)
+    d = len(vals[0])
+    return [sum(e[t] * vals[t][c] for t in range(len(vals))) / tot for c in range(d)]
+
+
+def _brute_decode(case, scale):
+    """Pure-Python paged decode: visit table entries in order, each block's
+    offsets in order, and stop at the context length."""
+    bs, hq, hkv = case["bs"], case["hq"], case["hkv"]
+    out = []
+    for s, T in enumerate(case["lens"]):
+        keys = [[] for _ in range(hkv)]
+        vals = [[] for _ in range(hkv)]
+        j = 0
+        while j * bs < T:
+            phys = int(case["tables"][s, j])
+            for o in range(bs):
+                if j * bs + o >= T:
+                    break
+                for g in range(hkv):
+                    keys[g].append(case["kc"][phys, g, o].tolist())
+                    vals[g].append(case["vc"][phys, g, o].tolist())
+            j += 1
+        row = []
+        for h in range(hq):
+            g = h * hkv // hq
+            if T == 0:
+                row.append([0.0] * case["d"])
+            else:
+                row.append(_brute_attend(case["q"][s, h].tolist(), keys[g], vals[g], scale))
+        out.append(row)
+    return np.array(out)
+
+
+def _sdpa(q, K, V, scale, causal=False):
+    """torch SDPA, float64, CPU, grouped-query heads by the library's own rule.
+    q: [Hq][Lq][d], K/V: [Hkv][Lk][d]."""
+    qt = torch.tensor(q, dtype=torch.float64)[None]
+    kt = torch.tensor(K, dtype=torch.float64)[None]
+    vt = torch.tensor(V, dtype=torch.float64)[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, is_causal=causal,
+                                       enable_gqa=True)
+    return o[0].numpy()
+
+
+# ------------------------------------------------------------- accounting
+
+def pin_kv_size(acct):
+    g = _golden("kv_cache_size.json")
+    m = acct.kv_cache_bytes(**g["inputs"])
+    assert round(m / 1e9, 2) == g["printed_approx"], m
+    assert m / 2 ** 30 == g["printed_half_gigabyte_binary"], m
+    # Linear in every factor (doubling any one doubles M), zero with no tokens.
+    base = g["inputs"]
+    for key in base:
+        twice = dict(base)
+        twice[key] = 2 * base[key]
+        assert acct.kv_cache_bytes(**twice) == 2 * m
+    assert acct.kv_cache_bytes(16, 4, 256, 0, 2) == 0
+
+
+def pin_worked_example_accounting(acct):
+    g = _golden("worked_example.json")
+    r, u, w = acct.contiguous_reservation(g["requests_tokens"], g["max_len"])
+    c = g["contiguous"]
+    assert (r, u, w) == (c["reserved"], c["used"], c["unused"])
+    assert round(100 * w / r) == c["waste_percent_printed"]
+    r2, u2, w2 = acct.paged_reservation(g["requests_tokens"], g["block_size"])
+    p = g["paged"]
+    assert (r2, u2, w2) == (p["reserved"], p["used"], p["unused"])
+    assert [acct.blocks_needed(t, g["block_size"]) * g["block_size"]
+            for t in g["requests_tokens"]] == p["per_request_slots"]
+    assert r - r2 == p["freed_vs_contiguous"]
+
+
+# -------------------------------------------------------------- allocator
+
+def pin_worked_example_allocator(alloc):
+    g = _golden("worked_example.json")
+    bs = g["block_size"]
+    pool = g["contiguous"]["reserved"] // bs
+    a = alloc.BlockAllocatorModel(pool, bs)
+    # Tokens arrive one at a time; blocks are handed out only when needed.
+    for step in range(max(g["requests_tokens"])):
+        for sid, n in enumerate(g["requests_tokens"]):
+            if step < n:
+                a.append(sid, 1)
+    held = [len(a.tables[s]) * bs for s in range(3)]
+    assert held == g["paged"]["per_request_slots"]
+    assert sum(held) == g["paged"]["reserved"]
+    assert a.num_free() * bs == g["paged"]["freed_vs_contiguous"]
+
+
+def _check_allocator_state(a, bs):
+    seen = set()
+    for sid, table in a.tables.items():
+        n = a.lengths[sid]
+        assert len(table) == (n + bs - 1) // bs          # on demand: no spare blocks
+        assert len(table) * bs - n < bs                   # only the last block has holes
+        for b in table:
+            assert b not in seen
+            seen.add(b)
+    assert not seen & set(a.free_blocks)
+    assert len(seen) + a.num_free() == a.num_blocks
+
+
+def pin_allocator_invariants(alloc):
+    rng = random.Random(7)
+    bs, nb = 4, 40
+    order = list(range(nb))
+    rng.shuffle(order)
+    a = alloc.BlockAllocatorModel(nb, bs, initial_order=order)
+    # The first blocks handed out follow the given free order.
+    s0 = a.append(100, 9)
+    assert a.tables[100] == order[:3]
+    assert s0 == [order[p // bs] * bs + p % bs for p in range(9)]
+    a.free(100)
+    assert list(a.free_blocks)[-3:] == order[:3]          # released to the back (FIFO)
+    live = {}
+    for step in range(400):
+        op = rng.random()
+        if op < 0.6 or not live:
+            sid = rng.randrange(12)
+            n = rng.randint(1, 9)
+            before = (list(a.free_blocks), {k: list(v) for k, v in a.tables.items()},
+                      dict(a.lengths))
+            try:
+                slots = a.append(sid, n)
+            except alloc.OutOfBlocks:
+                # atomic: nothing changed
+                assert before == (list(a.free_blocks),
+                                  {k: list(v) for k, v in a.tables.items()}, dict(a.lengths))
+                continue
+            start = a.lengths[sid] - n
+            table = a.tables[sid]
+            for i, slot in enumerate(slots):
+                pos = start + i
+                assert slot // bs == table[pos // bs] and slot % bs == pos % bs
+            live[sid] = True
+        else:
+            sid = rng.choice(sorted(live))
+            freed = list(a.tables[sid])
+            head = list(a.free_blocks)
+            a.free(sid)
+            del live[sid]
+            assert list(a.free_blocks) == head + freed
+        _check_allocator_state(a, bs)
+    # exhausting the pool raises and leaves the state intact
+    b = alloc.BlockAllocatorModel(3, 4)
+    b.append(1, 12)
+    try:
+        b.append(2, 1)
+        raise AssertionError("expected OutOfBlocks")
+    except alloc.OutOfBlocks:
+        pass
+    assert b.num_free() == 0 and 2 not in b.tables
+
+
+# -------------------------------------------------------------- attention
+
+def pin_cache_write(attn):
+    rng = np.random.default_rng(3)
+    nb, hkv, bs, d = 6, 2, 4, 8
+    kc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
+    vc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
+    kc[4] = np.nan
+    slots = np.array([0, 7, 22, -1, 13], dtype=np.int64)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    k2, v2 = attn.cache_write(kc, vc, key, val, slots, bs)
+    flat_k = k2.transpose(0, 2, 1, 3).reshape(nb * bs, hkv, d)
+    flat_v = v2.transpose(0, 2, 1, 3).reshape(nb * bs, hkv, d)
+    touched = set()
+    for i, s in enumerate(slots.tolist()):
+        if s < 0:
+            continue
+        assert np.array_equal(flat_k[s], key[i]) and np.array_equal(flat_v[s], val[i])
+        touched.add(s)
+    ok = np.transpose(kc, (0, 2, 1, 3)).reshape(nb * bs, hkv, d)
+    for s in range(nb * bs):
+        if s not in touched:
+            assert np.array_equal(flat_k[s].view(np.uint32), ok[s].view(np.uint32))
+    assert np.isnan(k2[4]).all()
+
+
+def pin_decode_bruteforce(attn):
+    rng = random.Random(11)
+    for trial in range(12):
+        hkv = rng.choice([1, 2, 3])
+        hq = hkv * rng.choice([1, 2, 3])
+        bs = rng.choice([1, 2, 4])
+        d = rng.choice([2, 3, 5, 8])
+        case = _tiny_case(rng, rng.randint(1, 3), 9, hq, hkv, d, bs, zero_len=(trial == 5))
+        scale = rng.uniform(0.2, 1.5)
+        want = _brute_decode(case, scale)
+        got = attn.decode(case["q"], case["kc"], case["vc"], case["tables"], case["lens"], bs,
+                          scale)
+        assert np.abs(got - want).max() <= 1e-12, (trial, np.abs(got - want).max())
+
+
+def pin_decode_vs_library(attn):
+    """One block per sequence at a random physical ID reduces paged decode to
+    textbook attention, which torch computes with its own GQA rule."""
+    rng = np.random.default_rng(5)
+    for hq, hkv, d, T in [(4, 1, 16, 7), (6, 2, 8, 12), (24, 4, 32, 16), (3, 3, 4, 1)]:
+        bs = 16
+        nb = 5
+        phys = int(rng.integers(nb))
+        K = rng.standard_normal((hkv, T, d))
+        V = rng.standard_normal((hkv, T, d))
+        q = rng.standard_normal((hq, d))
+        kc = np.full((nb, hkv, bs, d), np.nan)
+        vc = np.full((nb, hkv, bs, d), np.nan)
+        kc[phys, :, :T] = K
+        vc[phys, :, :T] = V
+        scale = 1 / math.sqrt(d)
+        got = attn.decode(q[None], kc, vc, np.array([[phys]]), [T], bs, scale)[0]
+        want = _sdpa(q[:, None, :], K, V, scale)[:, 0, :]
+        assert np.abs(got - want).max() < 1e-12
+
+
+def pin_decode_special_cases(attn):
+    rng = np.random.default_rng(9)
+    hq, hkv, d, bs = 6, 2, 8, 4
+    nb = 8
+    kc = rng.standard_normal((nb, hkv, bs, d))
+    vc = rng.standard_normal((nb, hkv, bs, d))
+    tables = np.array([[3, 1, 6], [0, 5, 2]])
+    q = rng.standard_normal((2, hq, d))
+    # one token: the output is that token's V exactly
+    out = attn.decode(q, kc, vc, tables, [1, 1], bs, 0.7)
+    for s in range(2):
+        for h in range(hq):
+            assert np.array_equal(out[s, h], vc[tables[s, 0], h // 3, 0])
+    # zero query: uniform weights -> mean of the V rows in context
+    out = attn.decode(np.zeros_like(q), kc, vc, tables, [10, 7], bs, 0.7)
+    for s, T in enumerate([10, 7]):
+        rows = [vc[tables[s, t // bs], :, t % bs] for t in range(T)]
+        assert np.abs(out[s, 0] - np.mean(rows, axis=0)[0]).max() < 1e-12
+        assert np.abs(out[s, 5] - np.mean(rows, axis=0)[1]).max() < 1e-12
+    # identical keys: uniform weights again, whatever q is
+    kc2 = np.broadcast_to(kc[0:1, :, 0:1, :], kc.shape).copy()
+    out = attn.decode(q, kc2, vc, tables, [9, 12], bs, 0.7)
+    rows = [vc[tables[1, t // bs], 1, t % bs] for t in range(12)]
+    assert np.abs(out[1, 4] - np.mean(rows, axis=0)).max() < 1e-12
+    # constant V: output equals the constant
+    vc3 = np.full_like(vc, 2.5)
+    out = attn.decode(q, kc, vc3, tables, [11, 5], bs, 0.7)
+    assert np.abs(out - 2.5).max() < 1e-12
+    # a huge scale turns softmax into a hard argmax over the keys
+    out = attn.decode(q, kc, vc, tables, [12, 12], bs, 1e4)
+    for s in range(2):
+        for h in range(hq):
+            g = h // 3
+            keys = [kc[tables[s, t // bs], g, t % bs] for t in range(12)]
+            best = int(np.argmax([k @ q[s, h] for k in keys]))
+            assert np.abs(out[s, h] - vc[tables[s, best // bs], g, best % bs]).max() < 1e-9
+
+
+def pin_permutation_invariance(attn):
+    rng = random.Random(21)
+    case = _tiny_case(rng, 3, 11, 4, 2, 5, 2, pool_extra=5)
+    base = attn.decode(case["q"], case["kc"], case["vc"], case["tables"], case["lens"], 2, 0.5)
+    nb = case["kc"].shape[0]
+    perm = list(range(nb))
+    rng.shuffle(perm)
+    kc = np.empty_like(case["kc"])
+    vc = np.empty_like(case["vc"])
+    for old, new in enumerate(perm):
+        kc[new] = case["kc"][old]
+        vc[new] = case["vc"][old]
+    tables = np.where(case["tables"] >= 0, np.array(perm)[case["tables"]], -1)
+    again = attn.decode(case["q"], kc, vc, tables, case["lens"], 2, 0.5)
+    assert np.array_equal(base, again)
+
+
+def pin_partitions(attn):
+    rng = random.Random(4)
+    case = _tiny_case(rng, 3, 23, 6, 3, 4, 2)
+    scale = 0.9
+    full = attn.decode(case["q"], case["kc"], case["vc"], case["tables"], case["lens"], 2, scale)
+    for P in [2, 4, 6, 8, 64]:
+        o, lse, n = attn.decode_partitions(case["q"], case["kc"], case["vc"], case["tables"],
+                                           case["lens"], 2, scale, P)
+        assert list(n) == [(t + P - 1) // P for t in case["lens"]]
+        merged = attn.merge_partitions(o, lse, n)
+        assert np.abs(merged - full).max() < 1e-12
+        # each partition's lse is log(sum(exp(logits))) over its own tokens
+        for s, T in enumerate(case["lens"]):
+            for h in range(6):
+                g = h // 2
+                for p in range(n[s]):
+                    logits = [scale * sum(a * b for a, b in
+                                          zip(case["q"][s, h].tolist(), case["K"][s][t][g]))
+                              for t in range(p * P, min(T, (p + 1) * P))]
+                    assert abs(lse[s, h, p] - math.log(sum(math.exp(z) for z in logits))) < 1e-12
+        if P == 64:   # one partition: o is the decode output itself
+            assert np.abs(o[:, :, 0, :] - full).max() < 1e-12
+    # very different partition scales: merge must not underflow
+    q = np.array(case["q"]) * 60.0
+    full = attn.decode(q, case["kc"], case["vc"], case["tables"], case["lens"], 2, scale)
+    o, lse, n = attn.decode_partitions(q, case["kc"], case["vc"], case["tables"], case["lens"],
+                                       2, scale, 4)
+    assert np.isfinite(full).all()
+    assert np.abs(attn.merge_partitions(o, lse, n) - full).max() < 1e-9
+
+
+def pin_prefill(attn):
+    rng = random.Random(8)
+    # no earlier context: causal textbook attention over the chunk (library)
+    case = _tiny_case(rng, 2, 10, 4, 2, 8, 4)
+    lens = case["lens"]
+    qsl = [0, lens[0], lens[0] + lens[1]]
+    nprng = np.random.default_rng(1)
+    q = nprng.standard_normal((qsl[-1], 4, 8))
+    out = attn.prefill(q, case["kc"], case["vc"], case["tables"], qsl, lens, 4, 0.35)
+    for s in range(2):
+        K = np.array(case["K"][s]).transpose(1, 0, 2)
+        V = np.array(case["V"][s]).transpose(1, 0, 2)
+        qs = q[qsl[s]:qsl[s + 1]].transpose(1, 0, 2)
+        want = _sdpa(qs, K, V, 0.35, causal=True).transpose(1, 0, 2)
+        assert np.abs(out[qsl[s]:qsl[s + 1]] - want).max() < 1e-12
+    # with earlier context: query j of a chunk of n sees the first T-n+j+1
+    # tokens, i.e. it equals decode over that prefix (brute force)
+    case = _tiny_case(rng, 3, 14, 6, 2, 4, 4)
+    chunks = [min(t, c) for t, c in zip(case["lens"], [3, 1, 5])]
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).tolist()
+    q = nprng.standard_normal((qsl[-1], 6, 4))
+    out = attn.prefill(q, case["kc"], case["vc"], case["tables"], qsl, case["lens"], 4, 0.6)
+    for s, T in enumerate(case["lens"]):
+        n = chunks[s]
+        for j in range(n):
+            sub = dict(case)
+            sub["lens"] = [T - n + j + 1]
+            sub["tables"] = case["tables"][s:s + 1]
+            sub["q"] = q[qsl[s] + j][None]
+            want = _brute_decode(sub, 0.6)[0]
+            assert np.abs(out[qsl[s] + j] - want).max() < 1e-12
+
+
+ATTENTION_PINS = [pin_cache_write, pin_decode_bruteforce, pin_decode_vs_library,
+                  pin_decode_special_cases, pin_permutation_invariance, pin_partitions,
+                  pin_prefill]
+ACCOUNTING_PINS = [pin_kv_size, pin_worked_example_accounting]
+ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants]

@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that at least one pin catches each. This shows the pins constrain every part
+of the oracle: a dropped term, a wrong sign or index, a swapped operand."""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as P
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+MUTATIONS = [
+    # (module, original text, planted mistake)
+    ("attention", "return h // (num_q_heads // num_kv_heads)", "return h % num_kv_heads"),
+    ("attention", "phys = int(block_table_row[t // block_size])",
+     "phys = int(block_table_row[t % block_size])"),
+    ("attention", "out[t] = cache[phys, :, t % block_size, :]",
+     "out[t] = cache[phys, :, t // block_size % cache.shape[2], :]"),
+    ("attention", "z = scale * (K @ q)", "z = K @ q"),
+    ("attention", "return (w @ V) / total, zmax + np.log(total)",
+     "return (w @ V), zmax + np.log(total)"),
+    ("attention", "return (w @ V) / total, zmax + np.log(total)",
+     "return (w @ V) / total, np.log(total)"),
+    ("attention", "w = np.exp(z - zmax)", "w = np.exp(zmax - z)"),
+    ("attention", "T = int(context_lens[s])\n        if T == 0:\n            continue\n        K = gather_context(key_cache, block_tables[s], T, block_size)\n        V = gather_context(value_cache, block_tables[s], T, block_size)\n        for h in range(num_q_heads):",
+     "T = int(context_lens[s]) - 1\n        if T <= 0:\n            continue\n        K = gather_context(key_cache, block_tables[s], T, block_size)\n        V = gather_context(value_cache, block_tables[s], T, block_size)\n        for h in range(num_q_heads):"),
+    ("attention", "lo, hi = p * partition_size, min(T, (p + 1) * partition_size)",
+     "lo, hi = p * partition_size, min(T, (p + 1) * partition_size - 1)"),
+    ("attention", "out[s, h] = (np.exp(l - total)[:, None] * o[s, h, :n]).sum(axis=0)",
+     "out[s, h] = (np.exp(l - top)[:, None] * o[s, h, :n]).sum(axis=0)"),
+    ("attention", "visible = T - n + j + 1", "visible = T - n + j"),
+    ("attention", "visible = T - n + j + 1", "visible = T"),
+    ("attention", "blk, off = slot // block_size, slot % block_size",
+     "off, blk = slot // block_size, slot % block_size"),
+    ("attention", "kc[blk, :, off, :] = key[i]", "kc[blk, :, off, :] = value[i]"),
+    ("accounting", "return 2 * num_layers * num_kv_heads", "return num_layers * num_kv_heads"),
+    ("accounting", "return -(-num_tokens // block_size)", "return num_tokens // block_size"),
+    ("accounting", "reserved = len(token_counts) * max_len", "reserved = sum(token_counts)"),
+    ("allocator", "table.append(self.free_blocks.popleft())",
+     "table.append(self.free_blocks.pop())"),
+    ("allocator", "self.free_blocks.extend(self.tables.pop(seq_id))",
+     "self.free_blocks.extendleft(self.tables.pop(seq_id))"),
+    ("allocator", "if want - have > len(self.free_blocks):", "if want - have > len(self.free_blocks) + 1:"),
+    ("allocator", "want = -(-(held + num_tokens) // self.block_size)",
+     "want = (held + num_tokens) // self.block_size + 1"),
+]
+
+PINS = {"attention": P.ATTENTION_PINS, "accounting": P.ACCOUNTING_PINS,
+        "allocator": P.ALLOCATOR_PINS}
+
+
+def _mutant(modname, old, new):
+    path = os.path.join(ORACLE_DIR, modname + ".py")
+    with open(path) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor not unique in {modname}: {old!r}"
+    mod = types.ModuleType("mutant_" + modname)
+    exec(compile(src.replace(old, new), path, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("modname,old,new", MUTATIONS,
+                         ids=[f"{m}:{n[:40]}" for m, _, n in MUTATIONS])
+def test_some_pin_catches_planted_mistake(modname, old, new):
+    mod = _mutant(modname, old, new)
+    caught = []
+    for pin in PINS[modname]:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {new!r}"
+
+
+def test_unmutated_copies_pass_every_pin():
+    for modname, pins in PINS.items():
+        mod = importlib.import_module("oracle." + modname)
+        for pin in pins:
+            pin(mod)
