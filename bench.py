@@ -1,0 +1,180 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+Workload (default): the mixed-length multi-tenant decode batch - 64 sequences
+with context lengths drawn log-uniform in [16, 8192], 24 query heads / 4 KV
+heads, head_dim 256, BF16, block_size 16, blocks scattered over a pool 1.5x
+the needed size - run as 16 independent layers back to back.
+
+One step = for each of the 16 layers: the slot-mapped write of the step's
+new K/V (pa_reshape_and_cache), split-context decode (pa_decode_partitioned,
+512-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
+slot mappings come from the host allocator's layout before timing starts;
+every input is resident in HBM when the timed region begins.
+
+Printed JSON (one line): value = effective KV read bandwidth of the whole
+step (exact context tokens x 4096 B per token per layer / step time); also
+tokens/s (64 new tokens per step), the decode kernel's roofline against
+8 TB/s HBM (its own launches timed with HIP events on the launch stream) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle sample (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(seed, budget_s):
+    """Time the fp64 oracle (write + decode) on whole sequences of one layer of
+    the same workload until the budget is spent; GB/s over the same
+    algorithmic KV bytes as the GPU figure."""
+    from oracle import attention as oracle
+    from paged_kv_cache_454_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    case = inputs.preset_case("mixed", seed=seed, garbage="random")
+    t0 = time.perf_counter()
+    done_tokens, done_seqs, passes = 0, 0, 0
+    while True:   # whole passes over the layer (write + decode of every sequence)
+        kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
+                                    case.slot_mapping, case.block_size)
+        oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens,
+                      case.block_size, case.scale)
+        done_tokens += int(case.context_lens.sum())
+        done_seqs += case.num_seqs
+        passes += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    gbs = done_tokens * 4096 / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} pass(es) over 1 layer of the mixed workload (slot write + "
+                      f"fp64 decode of all {case.num_seqs} sequences, {done_tokens} context "
+                      f"tokens in total) in {dt:.1f} s; decode tokens/s for a 16-layer step "
+                      f"{done_seqs / dt / 16:.3f}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    from paged_kv_cache_454_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers_n = inputs.PRESETS["mixed"]["layers"]
+    layers, meta = inputs.device_decode_layers("mixed", args.seed, layers_n, dev)
+    lens = meta["lens"]
+    P = args.partition_size
+    S = len(lens)
+    hq, d = layers[0]["query"].shape[1], layers[0]["query"].shape[2]
+    max_parts = max(1, math.ceil(int(lens.max()) / P))
+    po = torch.empty((S, hq, max_parts, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((S, hq, max_parts), dtype=torch.float32, device=dev)
+    ps = torch.empty((S, hq, max_parts), dtype=torch.float32, device=dev)
+    outs = [torch.empty((S, hq, d), dtype=torch.float32, device=dev) for _ in layers]
+    bt, cl, sm = meta["block_tables"], meta["context_lens"], meta["slot_mapping"]
+    scale = meta["scale"]
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        for li, L in enumerate(layers):
+            pa.pa_reshape_and_cache(L["key"], L["value"], L["key_cache"], L["value_cache"], sm,
+                                    stream=stream)
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
+                                     bt, cl, scale, P, stream=stream)
+            if record:
+                e1.record(stream)
+                ev.append((e0, e1))
+            pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(False)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # Decode-kernel launches timed on their own stream (a separate pass so the
+    # step timing above carries no event overhead).
+    torch.cuda.synchronize()
+    for _ in range(max(3, min(args.steps, 20))):
+        step(True)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(durs))
+
+    kv_bytes_layer = int(lens.sum()) * inputs.PRESETS["mixed"]["num_kv_heads"] * d * 2 * 2
+    step_bytes = kv_bytes_layer * layers_n
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    tok_s = S / (ms_step * 1e-3)
+    k_gbs = kv_bytes_layer / (kern_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), rounded to BF16)",
+        "config": {"workload": "mixed-length multi-tenant decode, 16 layers back to back",
+                   "num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
+                   "context_len_range": [int(lens.min()), int(lens.max())],
+                   "num_q_heads": hq, "num_kv_heads": 4, "head_dim": d, "block_size": 16,
+                   "pool_blocks": int(meta["num_blocks"]), "layers": layers_n,
+                   "partition_size": P, "seed": args.seed},
+        "tokens_per_s": round(tok_s, 1),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned",
+                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": kv_bytes_layer},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+/*
+ * pa.h - C ABI of libpa.so: paged KV cache writes, paged decode attention
+ * (single pass, and split-context partitions with a log-sum-exp reduce),
+ * chunked paged prefill, and a host-side block allocator, for AMD MI355X
+ * (gfx950).
+ *
+ * Sources the operations follow (cited by page title and section):
+ *  [P1] "High-Throughput LLM Inference & Training: A Deep Dive into vLLM"
+ *       (wpnews.pro), Fig. 1 and Fig. 2.
+ *  [P2] "vLLM Architecture, Memory and Benchmarks Deep Dive" (wpnews.pro),
+ *       sections 1-4.
+ *  [P3] "Optimizing LLM Inference: A Deep Dive into vLLM's PagedAttention and
+ *       Continuous Batching" (voronkin.com), KV-cache and PagedAttention
+ *       sections.
+ *  [P4] "Inside vLLM: Anatomy of a High-Throughput LLM Inference System"
+ *       (syntaxis blog), "Garbage Collection & Reuse", "FlashAttention-2
+ *       Integration".
+ *
+ * Conventions shared by every device entry point
+ * ----------------------------------------------
+ *  - Every tensor argument is a caller-owned, contiguous buffer; "[device]"
+ *    marks device memory on the current HIP device, "[host]" host memory.
+ *    The library never allocates, frees or keeps a pointer after returning.
+ *  - KV pools (one for keys, one for values), [P2] s.2 "fixed-size physical
+ *    blocks", [P3] "logical block ID mapped to a physical block ID":
+ *        key_cache, value_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ *    Logical position t of sequence s lives in physical block
+ *    block_tables[s][t / block_size] at offset t % block_size.
+ *  - block_tables : int32 [num_seqs][max_blocks_per_seq] ([P2] s.2 block
+ *    table); entries past a sequence's last block are never read.
+ *  - context_lens : int32 [num_seqs], tokens cached for each sequence,
+ *    counting the token written this step ([P2] s.1: the new token attends
+ *    over the cached K/V of the tokens before it and of itself).
+ *  - Grouped-query heads ([P2] s.1): query head h reads KV head
+ *    h / (num_q_heads / num_kv_heads).
+ *  - Calls are asynchronous and ordered on `stream` (0 = null stream).
+ *  - Host-checkable arguments are validated before anything is launched:
+ *    PA_EINVAL for bad sizes/pointers, PA_EUNSUPPORTED for shapes or dtypes
+ *    the kernels do not cover. pa_last_error() then describes the problem.
+ *  - Device-side contents are checked only as far as memory safety needs:
+ *    a block id outside [0, num_blocks) or a context longer than
+ *    max_blocks_per_seq * block_size never causes an out-of-range access; the
+ *    affected (sequence, head) outputs are set to NaN instead. A slot outside
+ *    [0, num_blocks * block_size) is not written.
+ *  - Nothing throws or aborts across the ABI.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = 1,        /* invalid argument (null pointer, bad size, ...)    */
+  PA_EUNSUPPORTED = 2,  /* valid, but a shape/dtype the kernels do not cover */
+  PA_ENOMEM = 3,        /* allocator: not enough free blocks                 */
+  PA_EHIP = 4,          /* a HIP runtime call failed (launch error, ...)     */
+  PA_ENOTFOUND = 5      /* allocator: unknown sequence id                    */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Message describing the last non-OK status returned on this thread
+ * ("" if none). The string stays valid until the next call on the thread. */
+const char *pa_last_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+const char *pa_version(void);
+
+/*
+ * pa_reshape_and_cache - slot-mapped write of this step's new K/V rows into
+ * the pools ([P2] s.1 KV caching; [P2] s.2 on-demand blocks: each new token
+ * goes to its sequence's last block).
+ *
+ *  key, value   [device] kv_dtype [num_tokens][num_kv_heads][head_dim]
+ *  key_cache,
+ *  value_cache  [device] kv_dtype pools (layout above), updated in place
+ *  slot_mapping [device] int64 [num_tokens]; slot = block * block_size +
+ *               offset. A negative slot skips the token.
+ * A bit copy: the pools receive the exact bits of key/value.
+ * num_tokens == 0 is a no-op. head_dim in [1, 1024].
+ */
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, pa_dtype kv_dtype,
+                               hipStream_t stream);
+
+/*
+ * pa_decode - single-pass paged decode attention: one query token per
+ * sequence attends over its whole paged context ([P3] PagedAttention section:
+ * the scattered blocks "appear contiguous to the attention mechanism").
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t][g]) V_s[t][g],
+ *   t < context_lens[s], g = h / (num_q_heads / num_kv_heads).
+ *
+ *  out          [device] out_dtype [num_seqs][num_q_heads][head_dim]
+ *  query        [device] kv_dtype  [num_seqs][num_q_heads][head_dim]
+ *  key_cache,
+ *  value_cache  [device] kv_dtype pools
+ *  block_tables [device] int32 [num_seqs][max_blocks_per_seq]
+ *  context_lens [device] int32 [num_seqs]; 0 gives an all-zero output row.
+ * One workgroup per (sequence, KV head); best when num_seqs * num_kv_heads
+ * is in the hundreds. For few long sequences use pa_decode_partitioned.
+ * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads <= 8;
+ * kv_dtype F32 or BF16; out_dtype F32 or BF16; any block_size >= 1.
+ */
+pa_status pa_decode(void *out, const void *query, const void *key_cache,
+                    const void *value_cache, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                    pa_dtype kv_dtype, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Bytes of fp32 workspace the split-context path needs:
+ * part_out [num_seqs][num_q_heads][max_parts][head_dim] plus
+ * part_max and part_sum [num_seqs][num_q_heads][max_parts] each.
+ * Returns 0 for non-positive arguments.
+ */
+size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_parts);
+
+/*
+ * pa_decode_partitioned - split-context decode. Partition p of sequence s
+ * covers positions [p*partition_size, min(T_s, (p+1)*partition_size)), where
+ * T_s = context_lens[s]; partitions p >= ceil(T_s / partition_size) are not
+ * written. For each (s, h, p) it writes
+ *   part_out[s][h][p][:] = softmax-weighted V over the partition (normalised
+ *                          within it),
+ *   part_max[s][h][p]    = m_p, the reference logit the partition's
+ *                          exponentials were taken against (close to its
+ *                          largest scaled logit),
+ *   part_sum[s][h][p]    = l_p = sum_t exp(logit_t - m_p) over the partition,
+ * so m_p + ln(l_p) is the partition's log-sum-exp (only that sum is unique).
+ *
+ *  part_out, part_max, part_sum [device] fp32, shapes above (see
+ *               pa_partition_workspace_bytes)
+ *  other arguments as pa_decode.
+ *  partition_size: multiple of block_size, >= 16.
+ *  max_parts >= ceil(max_s T_s / partition_size) (the caller's bound; a
+ *               longer context makes that sequence's outputs NaN).
+ */
+pa_status pa_decode_partitioned(float *part_out, float *part_max, float *part_sum,
+                                const void *query, const void *key_cache,
+                                const void *value_cache, const int32_t *block_tables,
+                                const int32_t *context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, float scale, int32_t partition_size,
+                                int32_t max_parts, pa_dtype kv_dtype, hipStream_t stream);
+
+/*
+ * pa_reduce - log-sum-exp merge of the partitions written by
+ * pa_decode_partitioned:
+ *   w_p = part_sum_p * exp(part_max_p - max_q part_max_q),
+ *   out[s][h] = sum_p w_p * part_out_p / sum_p w_p, p < ceil(T_s/partition_size).
+ *
+ *  out          [device] out_dtype [num_seqs][num_q_heads][head_dim]
+ *  part_*       [device] as written by pa_decode_partitioned
+ *  context_lens [device] int32 [num_seqs]; 0 gives an all-zero row.
+ */
+pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
+                    const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                    int32_t max_parts, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_prefill_chunk - chunked paged prefill ([P2] s.4 chunked prefill; [P4]
+ * "FlashAttention-2 Integration": causal attention over packed, unpadded
+ * queries). The chunk's own K/V must already be in the pools
+ * (pa_reshape_and_cache). Queries of sequence s are the packed rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1; with n_s rows they sit at
+ * positions T_s - n_s .. T_s - 1 (T_s = context_lens[s]) and query j attends
+ * causally to positions 0 .. T_s - n_s + j.
+ *
+ *  out             [device] out_dtype [num_q_tokens][num_q_heads][head_dim]
+ *  query           [device] kv_dtype  [num_q_tokens][num_q_heads][head_dim]
+ *  query_start_loc [device] int32 [num_seqs + 1], non-decreasing, starting at 0
+ *  context_lens    [device] int32 [num_seqs], T_s >= n_s (else NaN rows)
+ *  num_q_tokens    rows of query/out; rows at or past it are never touched
+ *  max_query_len   host bound on n_s (sizes the launch grid); queries past
+ *                  it are not computed
+ * Supported: kv_dtype BF16, head_dim 256 or 128 or 64, num_q_heads /
+ * num_kv_heads <= 8. Q.K^T and P.V run on the matrix cores (MFMA, fp32
+ * accumulation).
+ */
+pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *query_start_loc, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t num_q_tokens, int32_t max_query_len,
+                           int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                           pa_dtype kv_dtype, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Host block allocator ([P2] s.2 "On-Demand Allocation": blocks are handed
+ * out only as tokens arrive, so only a sequence's last block has unused
+ * slots; [P2] s.3: a finished sequence's blocks return to the pool at once;
+ * [P4] "Garbage Collection & Reuse": free blocks form a first-in first-out
+ * queue). Host memory only; not thread-safe (one allocator per thread or
+ * external locking). No device memory is touched.
+ */
+typedef struct pa_alloc pa_alloc;
+
+/* Create a pool of num_blocks blocks of block_size tokens. initial_order
+ * [host] int32 [num_blocks] is the initial free-queue order (a permutation of
+ * 0..num_blocks-1; NULL = 0, 1, 2, ...). On success *out owns the allocator. */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t *initial_order,
+                          pa_alloc **out);
+void pa_alloc_destroy(pa_alloc *a);
+
+/* Grow sequence seq_id (created on first use) by num_tokens tokens, taking
+ * blocks from the front of the free queue only when its last block is full.
+ * slots_out [host] int64 [num_tokens] or NULL receives each new token's slot.
+ * All or nothing: on PA_ENOMEM nothing changes. */
+pa_status pa_alloc_append(pa_alloc *a, int64_t seq_id, int32_t num_tokens, int64_t *slots_out);
+
+/* Return all blocks of seq_id to the back of the free queue (in the
+ * sequence's logical order) and forget it. PA_ENOTFOUND if unknown. */
+pa_status pa_alloc_free(pa_alloc *a, int64_t seq_id);
+
+/* Free blocks in the pool; -1 if a is NULL. */
+int32_t pa_alloc_num_free(const pa_alloc *a);
+
+/* Tokens held by seq_id, or -1 if unknown. */
+int32_t pa_alloc_seq_len(const pa_alloc *a, int64_t seq_id);
+
+/* Write block-table rows and context lengths for n sequences.
+ *  seq_ids   [host] int64 [n]
+ *  table_out [host] int32 [n][max_blocks], unused entries set to -1
+ *  lens_out  [host] int32 [n] or NULL
+ * PA_EINVAL if a sequence holds more than max_blocks blocks,
+ * PA_ENOTFOUND for an unknown id (outputs then unspecified). */
+pa_status pa_alloc_block_table(const pa_alloc *a, const int64_t *seq_ids, int32_t n,
+                               int32_t max_blocks, int32_t *table_out, int32_t *lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

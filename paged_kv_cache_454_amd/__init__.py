@@ -1,0 +1,12 @@
+"""Paged KV cache + PagedAttention decode for AMD MI355X (gfx950).
+
+The compute path is libpa.so (hand-written HIP kernels behind a C ABI,
+``include/pa.h``); this package only loads it and marshals torch tensors to
+it (``binding``). ``inputs`` holds the seeded synthetic workloads.
+"""
+
+from .binding import (BlockAllocator, PAError, pa_decode, pa_decode_partitioned,  # noqa: F401
+                      pa_partition_workspace_bytes, pa_prefill_chunk, pa_reduce,
+                      pa_reshape_and_cache)
+
+__version__ = "0.1.0"

@@ -1,0 +1,220 @@
+"""Python binding of libpa.so with the C ABI's names.
+
+Marshalling only: each function reads shapes, dtypes and device pointers off
+torch tensors, checks that they are consistent (so the C side is handed the
+true sizes of every buffer), passes the current HIP stream, calls the C entry
+point and raises ``PAError`` on a non-OK status. Every step of the path runs
+in the library's kernels; nothing here computes.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import PA_BF16, PA_F32, PAError, check, lib  # noqa: F401
+
+_DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+def _dtype(t, what):
+    if t.dtype not in _DT:
+        raise ValueError(f"{what}: dtype {t.dtype} (supported: float32, bfloat16)")
+    return _DT[t.dtype]
+
+
+def _dev(t, what, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{what}: {t.dim()} dims, expected {ndim}")
+    if t.data_ptr() % 16 != 0 and t.numel() > 0:
+        raise ValueError(f"{what}: data pointer must be 16-byte aligned")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _pool_shape(key_cache, value_cache):
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must match in shape and dtype")
+    if key_cache.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    return key_cache.shape
+
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """Write key/value [num_tokens][H_KV][d] into the pools at slot_mapping."""
+    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens][num_kv_heads][head_dim] matching the pools")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise ValueError("key/value dtype must match the pools")
+    n = key.shape[0]
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != n:
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    args = [_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64)]
+    check(lib().pa_reshape_and_cache(*args, n, hkv, d, bs, num_blocks,
+                                     _dtype(key_cache, "pools"), _stream(stream)))
+
+
+def _attn_common(query, key_cache, value_cache, block_tables, context_lens, rows_name):
+    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != d:
+        raise ValueError(f"query must be [{rows_name}][num_q_heads][{d}]")
+    if query.dtype != key_cache.dtype:
+        raise ValueError("query dtype must match the pools")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [num_seqs][max_blocks_per_seq]")
+    num_seqs = block_tables.shape[0]
+    if context_lens.dim() != 1 or context_lens.shape[0] != num_seqs:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    return num_blocks, hkv, bs, d, num_seqs
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+              stream=None):
+    """Single-pass paged decode; out [num_seqs][H_q][d] (float32 or bfloat16)."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    if query.shape[0] != num_seqs or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("query/out must be [num_seqs][num_q_heads][head_dim]")
+    hq = query.shape[1]
+    check(lib().pa_decode(_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+                          _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+                          context_lens.data_ptr(), num_seqs, hq, hkv, d, bs,
+                          block_tables.shape[1], num_blocks, float(scale),
+                          _dtype(key_cache, "pools"), _dtype(out, "out"), _stream(stream)))
+
+
+def pa_partition_workspace_bytes(num_seqs, num_q_heads, head_dim, max_parts):
+    return int(lib().pa_partition_workspace_bytes(num_seqs, num_q_heads, head_dim, max_parts))
+
+
+def pa_decode_partitioned(part_out, part_max, part_sum, query, key_cache, value_cache,
+                          block_tables, context_lens, scale, partition_size, stream=None):
+    """Split-context decode into part_out [S][H_q][P][d], part_max/part_sum [S][H_q][P]."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    hq = query.shape[1]
+    if query.shape[0] != num_seqs:
+        raise ValueError("query must be [num_seqs][num_q_heads][head_dim]")
+    if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (num_seqs, hq) or part_out.shape[3] != d:
+        raise ValueError("part_out must be float32 [num_seqs][num_q_heads][max_parts][head_dim]")
+    max_parts = part_out.shape[2]
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (num_seqs, hq, max_parts):
+            raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
+    check(lib().pa_decode_partitioned(
+        _dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
+        _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
+        float(scale), int(partition_size), max_parts, _dtype(key_cache, "pools"),
+        _stream(stream)))
+
+
+def pa_reduce(out, part_out, part_max, part_sum, context_lens, partition_size, stream=None):
+    """Log-sum-exp merge of partitions into out [num_seqs][H_q][d]."""
+    if part_out.dim() != 4:
+        raise ValueError("part_out must be [num_seqs][num_q_heads][max_parts][head_dim]")
+    num_seqs, hq, max_parts, d = part_out.shape
+    if tuple(out.shape) != (num_seqs, hq, d):
+        raise ValueError("out must be [num_seqs][num_q_heads][head_dim]")
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (num_seqs, hq, max_parts):
+            raise ValueError(f"{nm} must be [num_seqs][num_q_heads][max_parts]")
+    if context_lens.dim() != 1 or context_lens.shape[0] != num_seqs:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    check(lib().pa_reduce(_dev(out, "out"), _dev(part_out, "part_out", torch.float32),
+                          _dev(part_max, "part_max", torch.float32),
+                          _dev(part_sum, "part_sum", torch.float32),
+                          _dev(context_lens, "context_lens", torch.int32), num_seqs, hq, d,
+                          int(partition_size), max_parts, _dtype(out, "out"), _stream(stream)))
+
+
+def pa_prefill_chunk(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                     context_lens, max_query_len, scale, stream=None):
+    """Causal chunked prefill; query/out packed [num_q_tokens][H_q][d]."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_q_tokens")
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must match query's shape")
+    if query_start_loc.dim() != 1 or query_start_loc.shape[0] != num_seqs + 1:
+        raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
+    hq = query.shape[1]
+    check(lib().pa_prefill_chunk(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        _dev(query_start_loc, "query_start_loc", torch.int32), context_lens.data_ptr(),
+        num_seqs, query.shape[0], int(max_query_len), hq, hkv, d, bs, block_tables.shape[1],
+        num_blocks, float(scale), _dtype(key_cache, "pools"), _dtype(out, "out"),
+        _stream(stream)))
+
+
+class BlockAllocator:
+    """Owner of a host ``pa_alloc``: on-demand blocks from a FIFO free queue."""
+
+    def __init__(self, num_blocks, block_size, initial_order=None):
+        h = ctypes.c_void_p()
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_order must have num_blocks entries")
+        check(lib().pa_alloc_create(num_blocks, block_size,
+                                    None if order is None else order.ctypes.data,
+                                    ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().pa_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, seq_id, num_tokens):
+        """Grow a sequence; returns the new tokens' slots (int64 numpy array)."""
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        check(lib().pa_alloc_append(self._h, int(seq_id), int(num_tokens),
+                                    slots.ctypes.data if num_tokens > 0 else None))
+        return slots
+
+    def free(self, seq_id):
+        check(lib().pa_alloc_free(self._h, int(seq_id)))
+
+    def num_free(self):
+        return int(lib().pa_alloc_num_free(self._h))
+
+    def seq_len(self, seq_id):
+        return int(lib().pa_alloc_seq_len(self._h, int(seq_id)))
+
+    def block_table(self, seq_ids, max_blocks):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        table = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        check(lib().pa_alloc_block_table(self._h, ids.ctypes.data if len(ids) else None, len(ids),
+                                         max_blocks, table.ctypes.data, lens.ctypes.data))
+        return table, lens

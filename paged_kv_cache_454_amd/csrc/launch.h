@@ -1,0 +1,73 @@
+// Internal launchers called by the C entry points after argument checks.
+#pragma once
+
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+pa_status launch_cache_write(const void *key, const void *value, void *key_cache,
+                             void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int elem_bytes, hipStream_t stream);
+
+// Arguments of the decode kernels (single pass when partition_size == 0).
+struct DecodeParams {
+  const void *query;
+  const void *key_cache;
+  const void *value_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start_loc;  // non-null: causal prefill rows (generic kernel only)
+  int32_t max_query_len;           // prefill: bound on rows per sequence
+  int32_t num_q_tokens;            // prefill: rows of query / out
+  void *out;          // single pass: [num_seqs][num_q_heads][head_dim], out dtype
+  float *part_out;    // partitioned: [num_seqs][num_q_heads][max_parts][head_dim]
+  float *part_max;    // partitioned: [num_seqs][num_q_heads][max_parts]
+  float *part_sum;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  float scale;
+  int32_t partition_size;  // 0 = single pass
+  int32_t max_parts;       // 1 for single pass
+  int32_t kv_bf16;
+  int32_t out_bf16;
+};
+
+pa_status launch_decode(const DecodeParams &p, hipStream_t stream);
+
+pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
+                        const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                        int32_t max_parts, int32_t out_bf16, hipStream_t stream);
+
+struct PrefillParams {
+  void *out;
+  const void *query;
+  const void *key_cache;
+  const void *value_cache;
+  const int32_t *block_tables;
+  const int32_t *query_start_loc;
+  const int32_t *context_lens;
+  int32_t num_seqs;
+  int32_t num_q_tokens;
+  int32_t max_query_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  float scale;
+  int32_t out_bf16;
+};
+
+pa_status launch_prefill(const PrefillParams &p, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,218 @@
+// C entry points: host-side argument checks, then the kernel launchers.
+#include <math.h>
+
+#include "launch.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_BF16; }
+int dtype_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
+
+// Shared checks of the paged-attention shapes.
+pa_status check_attention_shape(const char *fn, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                                pa_dtype kv_dtype) {
+  if (num_seqs < 0) return pa::fail(PA_EINVAL, "%s: num_seqs=%d < 0", fn, num_seqs);
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return pa::fail(PA_EINVAL, "%s: head counts must be > 0 (q=%d kv=%d)", fn, num_q_heads,
+                    num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return pa::fail(PA_EINVAL, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", fn,
+                    num_q_heads, num_kv_heads);
+  if (head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return pa::fail(PA_EINVAL,
+                    "%s: head_dim=%d block_size=%d max_blocks_per_seq=%d num_blocks=%d must be > 0",
+                    fn, head_dim, block_size, max_blocks_per_seq, num_blocks);
+  if (!isfinite(scale)) return pa::fail(PA_EINVAL, "%s: scale is not finite", fn);
+  if (!dtype_ok(kv_dtype)) return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return pa::fail(PA_EUNSUPPORTED, "%s: head_dim=%d (supported: 64, 128, 256)", fn, head_dim);
+  if (num_q_heads / num_kv_heads > 8)
+    return pa::fail(PA_EUNSUPPORTED, "%s: query heads per KV head = %d > 8", fn,
+                    num_q_heads / num_kv_heads);
+  if ((int64_t)max_blocks_per_seq * block_size > 0x7fffffff)
+    return pa::fail(PA_EUNSUPPORTED, "%s: max_blocks_per_seq * block_size exceeds 2^31", fn);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                                          void *value_cache, const int64_t *slot_mapping,
+                                          int32_t num_tokens, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int32_t num_blocks, pa_dtype kv_dtype,
+                                          hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_reshape_and_cache";
+  if (num_tokens < 0) return pa::fail(PA_EINVAL, "%s: num_tokens=%d < 0", fn, num_tokens);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa::fail(PA_EINVAL, "%s: num_kv_heads=%d head_dim=%d block_size=%d num_blocks=%d", fn,
+                    num_kv_heads, head_dim, block_size, num_blocks);
+  if (head_dim > 1024) return pa::fail(PA_EUNSUPPORTED, "%s: head_dim=%d > 1024", fn, head_dim);
+  if (!dtype_ok(kv_dtype)) return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  return pa::launch_cache_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                num_kv_heads, head_dim, block_size, num_blocks,
+                                dtype_bytes(kv_dtype), stream);
+}
+
+extern "C" pa_status pa_decode(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                               pa_dtype kv_dtype, pa_dtype out_dtype, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = 0;
+  p.max_parts = 1;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.out_bf16 = out_dtype == PA_BF16;
+  return pa::launch_decode(p, stream);
+}
+
+extern "C" size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t max_parts) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_parts <= 0) return 0;
+  const size_t n = (size_t)num_seqs * num_q_heads * max_parts;
+  return n * (size_t)head_dim * sizeof(float) + 2 * n * sizeof(float);
+}
+
+extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, float *part_sum,
+                                           const void *query, const void *key_cache,
+                                           const void *value_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                                           float scale, int32_t partition_size,
+                                           int32_t max_parts, pa_dtype kv_dtype,
+                                           hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_partitioned";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size % block_size != 0)
+    return pa::fail(PA_EINVAL, "%s: partition_size=%d must be >= 16 and a multiple of block_size=%d",
+                    fn, partition_size, block_size);
+  if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
+  if (num_seqs == 0) return PA_OK;
+  if (!part_out || !part_max || !part_sum || !query || !key_cache || !value_cache ||
+      !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = partition_size;
+  p.max_parts = max_parts;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
+                               const float *part_sum, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t partition_size, int32_t max_parts, pa_dtype out_dtype,
+                               hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_reduce";
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0 || max_parts <= 0)
+    return pa::fail(PA_EINVAL,
+                    "%s: num_seqs=%d num_q_heads=%d head_dim=%d partition_size=%d max_parts=%d",
+                    fn, num_seqs, num_q_heads, head_dim, partition_size, max_parts);
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !part_out || !part_max || !part_sum || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  return pa::launch_reduce(out, part_out, part_max, part_sum, context_lens, num_seqs, num_q_heads,
+                           head_dim, partition_size, max_parts, out_dtype == PA_BF16, stream);
+}
+
+extern "C" pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const int32_t *block_tables,
+                                      const int32_t *query_start_loc, const int32_t *context_lens,
+                                      int32_t num_seqs, int32_t num_q_tokens,
+                                      int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t num_blocks, float scale, pa_dtype kv_dtype,
+                                      pa_dtype out_dtype, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_prefill_chunk";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (kv_dtype != PA_BF16) return pa::fail(PA_EUNSUPPORTED, "%s: kv_dtype must be BF16", fn);
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  if (max_query_len < 0 || num_q_tokens < 0)
+    return pa::fail(PA_EINVAL, "%s: max_query_len=%d num_q_tokens=%d", fn, max_query_len,
+                    num_q_tokens);
+  if (num_seqs == 0 || max_query_len == 0 || num_q_tokens == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
+      !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::PrefillParams p{};
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.query_start_loc = query_start_loc;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_tokens = num_q_tokens;
+  p.max_query_len = max_query_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.out_bf16 = out_dtype == PA_BF16;
+  return pa::launch_prefill(p, stream);
+}

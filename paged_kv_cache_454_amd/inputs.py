@@ -121,7 +121,30 @@ def _scatter_tables(rng, blocks_per_seq, num_blocks):
     return tables
 
 
-def _mark_garbage(pool, tables, filled, block_size, garbage, rng):
+def _layout(rng, lens, block_size, pool_factor, num_blocks):
+    """Block tables (seeded scatter) and the slot of each sequence's newest
+    token, position T_s - 1 (the token this decode step writes)."""
+    bps = [_ceil_div(t, block_size) for t in lens]
+    if num_blocks is None:
+        num_blocks = max(1, int(math.ceil(pool_factor * sum(bps))))
+    tables = _scatter_tables(rng, bps, num_blocks)
+    slots = np.full(len(lens), -1, dtype=np.int64)
+    for s in range(len(lens)):
+        if lens[s] > 0:
+            pos = int(lens[s]) - 1
+            slots[s] = int(tables[s, pos // block_size]) * block_size + pos % block_size
+    return tables, slots, num_blocks
+
+
+def decode_layout(context_lens, block_size, pool_factor=1.0, num_blocks=None, seed=0):
+    """Only the integer layout of :func:`decode_case` (same seed -> same
+    tables and slots): (block_tables, slot_mapping, num_blocks)."""
+    rng = np.random.default_rng(seed)
+    return _layout(rng, np.asarray(context_lens, dtype=np.int64), block_size, pool_factor,
+                   num_blocks)
+
+
+def _mark_garbage(pool, tables, filled, block_size, garbage):
     """Slots that hold no token (unused blocks, tails, this step's targets)
     become NaN ('nan') or keep their random draw ('random')."""
     if garbage == "random":
@@ -164,11 +187,7 @@ def decode_case(context_lens, num_q_heads, num_kv_heads, head_dim, block_size, d
     """
     rng = np.random.default_rng(seed)
     lens = np.asarray(context_lens, dtype=np.int64)
-    bps = [_ceil_div(t, block_size) for t in lens]
-    need = sum(bps)
-    if num_blocks is None:
-        num_blocks = max(1, int(math.ceil(pool_factor * need)))
-    tables = _scatter_tables(rng, bps, num_blocks)
+    tables, slots, num_blocks = _layout(rng, lens, block_size, pool_factor, num_blocks)
     if max_blocks_per_seq is not None and max_blocks_per_seq > tables.shape[1]:
         pad = np.full((tables.shape[0], max_blocks_per_seq - tables.shape[1]), -1, np.int32)
         tables = np.concatenate([tables, pad], axis=1)
@@ -186,13 +205,8 @@ def decode_case(context_lens, num_q_heads, num_kv_heads, head_dim, block_size, d
     elif dtype != "f32":
         raise ValueError(dtype)
     # Before the write each sequence holds all but its newest token.
-    _mark_garbage(kc, tables, lens - 1, block_size, garbage, rng)
-    _mark_garbage(vc, tables, lens - 1, block_size, garbage, rng)
-    slots = np.full(B, -1, dtype=np.int64)
-    for s in range(B):
-        if lens[s] > 0:
-            pos = int(lens[s]) - 1
-            slots[s] = int(tables[s, pos // block_size]) * block_size + pos % block_size
+    _mark_garbage(kc, tables, lens - 1, block_size, garbage)
+    _mark_garbage(vc, tables, lens - 1, block_size, garbage)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     return PagedCase(name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads,
@@ -227,8 +241,8 @@ def prefill_case(existing_lens, chunk_lens, num_q_heads, num_kv_heads, head_dim,
     q = rng.standard_normal((n_new, num_q_heads, head_dim), dtype=np.float32)
     if dtype == "bf16":
         kc, vc, new_k, new_v, q = (round_to_bf16(a) for a in (kc, vc, new_k, new_v, q))
-    _mark_garbage(kc, tables, ex, block_size, garbage, rng)
-    _mark_garbage(vc, tables, ex, block_size, garbage, rng)
+    _mark_garbage(kc, tables, ex, block_size, garbage)
+    _mark_garbage(vc, tables, ex, block_size, garbage)
     qsl = np.zeros(len(lens) + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(ch)
     slots = np.empty(n_new, dtype=np.int64)
@@ -279,3 +293,47 @@ def preset_case(name, seed=0, garbage="nan"):
     return prefill_case(ex, [chunk] * len(ex), p["num_q_heads"], p["num_kv_heads"],
                         p["head_dim"], p["block_size"], dtype=p["dtype"], seed=seed,
                         garbage=garbage, name=name)
+
+
+def device_decode_layers(name, seed, layers, device, dtype=None):
+    """Full-size decode workload generated on the device for timing: one
+    shared block table / slot mapping (a block table per sequence, as for a
+    real model's layers) and, per layer, its own K/V pools, query and new
+    K/V drawn N(0,1) (plus the preset's per-head bias) with a seeded torch
+    generator, rounded to BF16. Garbage slots keep their random draws."""
+    import torch
+    p = PRESETS[name]
+    lens = preset_lengths(name, seed)
+    tables, slots, num_blocks = decode_layout(lens, p["block_size"],
+                                              pool_factor=p.get("pool_factor", 1.0),
+                                              num_blocks=p.get("num_blocks"), seed=seed)
+    dt = dtype or (torch.bfloat16 if p["dtype"] == "bf16" else torch.float32)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    hq, hkv, d, bs = p["num_q_heads"], p["num_kv_heads"], p["head_dim"], p["block_size"]
+    B = len(lens)
+    bias = p.get("kv_bias_scale", 0.0)
+    out = []
+    for _ in range(layers):
+        layer = {}
+        for nm, shape in (("key_cache", (num_blocks, hkv, bs, d)),
+                          ("value_cache", (num_blocks, hkv, bs, d)),
+                          ("key", (B, hkv, d)), ("value", (B, hkv, d)), ("query", (B, hq, d))):
+            x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            layer[nm] = x
+        if bias:
+            bk = bias * torch.randn((hkv, d), generator=g, device=device)
+            bv = bias * torch.randn((hkv, d), generator=g, device=device)
+            layer["key_cache"] += bk[None, :, None, :]
+            layer["value_cache"] += bv[None, :, None, :]
+            layer["key"] += bk[None]
+            layer["value"] += bv[None]
+        out.append({k: v.to(dt) for k, v in layer.items()})
+        del layer
+    meta = dict(
+        context_lens=torch.from_numpy(lens.astype(np.int32)).to(device),
+        block_tables=torch.from_numpy(tables).to(device),
+        slot_mapping=torch.from_numpy(slots).to(device),
+        lens=lens, num_blocks=num_blocks, scale=p.get("scale") or 1.0 / math.sqrt(d),
+        partition_size=p.get("partition_size", 512))
+    return out, meta
