@@ -26,6 +26,11 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+WORKLOAD_NAMES = {
+    "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
+    "long": "long-context split decode, 4 seqs {8192, 16384, 32768, 32768}, bs 32",
+    "uniform": "uniform decode, 8 seqs x 2048, bs 16",
+}
 
 
 def parse():
@@ -35,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--workload", default="mixed", choices=["mixed", "long", "uniform"],
+                    help="decode workload (default: the mixed-length 16-layer batch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
     return ap.parse_args()
@@ -87,8 +94,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layers_n = inputs.PRESETS["mixed"]["layers"]
-    layers, meta = inputs.device_decode_layers("mixed", args.seed, layers_n, dev)
+    W = args.workload
+    layers_n = inputs.PRESETS[W].get("layers", 1)
+    layers, meta = inputs.device_decode_layers(W, args.seed, layers_n, dev)
     lens = meta["lens"]
     P = args.partition_size
     S = len(lens)
@@ -138,7 +146,8 @@ def main():
     durs = [a.elapsed_time(b) for a, b in ev]
     kern_ms = float(np.mean(durs))
 
-    kv_bytes_layer = int(lens.sum()) * inputs.PRESETS["mixed"]["num_kv_heads"] * d * 2 * 2
+    hkv = inputs.PRESETS[W]["num_kv_heads"]
+    kv_bytes_layer = int(lens.sum()) * hkv * d * 2 * 2
     step_bytes = kv_bytes_layer * layers_n
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     tok_s = S / (ms_step * 1e-3)
@@ -157,10 +166,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), rounded to BF16)",
-        "config": {"workload": "mixed-length multi-tenant decode, 16 layers back to back",
+        "config": {"workload": WORKLOAD_NAMES[W],
                    "num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
                    "context_len_range": [int(lens.min()), int(lens.max())],
-                   "num_q_heads": hq, "num_kv_heads": 4, "head_dim": d, "block_size": 16,
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                   "block_size": inputs.PRESETS[W]["block_size"],
                    "pool_blocks": int(meta["num_blocks"]), "layers": layers_n,
                    "partition_size": P, "seed": args.seed},
         "tokens_per_s": round(tok_s, 1),
@@ -171,7 +181,7 @@ def main():
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and W == "mixed":
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-HIP_SOURCES = ["cache_write.hip", "decode.hip", "reduce.hip", "prefill.hip", "pa_api.hip"]
+HIP_SOURCES = ["cache_write.hip", "decode.hip", "decode_tiled.hip", "reduce.hip", "prefill.hip",
+               "pa_api.hip"]
 HOST_SOURCES = ["errors.cpp", "alloc.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

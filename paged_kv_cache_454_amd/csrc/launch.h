@@ -42,6 +42,10 @@ struct DecodeParams {
 
 pa_status launch_decode(const DecodeParams &p, hipStream_t stream);
 
+// Specialised decode for BF16, head_dim 256, block_size % 16 == 0 (decode
+// rows only). Returns false when the shape is not covered.
+bool launch_decode_tiled(const DecodeParams &p, unsigned grid, hipStream_t stream);
+
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

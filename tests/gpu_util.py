@@ -43,12 +43,18 @@ def write(t):
                             t["slot_mapping"])
 
 
-def bits(x):
-    """Host uint32 bit patterns of a float tensor/array after widening to fp32
-    (bf16 -> fp32 is exact, so equal bits here mean equal bf16 bits)."""
-    if isinstance(x, torch.Tensor):
-        x = x.detach().to(torch.float32).cpu().numpy()
-    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+def bits(x, dtype=None):
+    """Host bit patterns of a tensor/array in the storage dtype: device
+    tensors as they are; host float32 arrays after the same torch conversion
+    that produced the device inputs (so NaN garbage compares equal)."""
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        if dtype is not None:
+            x = x.to(dtype)
+    x = x.detach().contiguous().cpu()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy()
+    return x.to(torch.float32).numpy().view(np.uint32)
 
 
 def decode(t, case, out_dtype=torch.float32):

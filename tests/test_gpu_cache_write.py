@@ -18,8 +18,9 @@ def _check_write(case):
     torch.cuda.synchronize()
     kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
                                 case.slot_mapping, case.block_size)
-    assert np.array_equal(G.bits(t["key_cache"]), G.bits(kc))
-    assert np.array_equal(G.bits(t["value_cache"]), G.bits(vc))
+    dt = G.torch_dtype(case)
+    assert np.array_equal(G.bits(t["key_cache"]), G.bits(kc, dt))
+    assert np.array_equal(G.bits(t["value_cache"]), G.bits(vc, dt))
     return t
 
 
