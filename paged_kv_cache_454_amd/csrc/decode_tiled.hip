@@ -36,8 +36,11 @@
 //    accumulators.
 //  * The two token halves of the wavefront are merged with
 //    v_permlane32_swap, the NW wavefronts through LDS.
-// Out-of-range tokens of a partial tile are masked with selects (their slots
-// may hold NaN garbage): logits to -inf, V rows to 0.
+// Out-of-range tokens of a partial tile (their slots may hold NaN garbage)
+// never reach the arithmetic: their logits are set to -inf with selects, and
+// their K/V rows lie past the tile resource's num_records, so the buffer
+// loads return zeros for them (the whole byte offset is a vector offset,
+// which the range check covers).
 #include <math.h>
 
 #include "launch.h"
@@ -101,8 +104,8 @@ template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_tiled_kernel(DecodeParams p) {
   using C = Tiled<G, NW>;
-  __shared__ float red_all[NW][C::RED];
-  __shared__ uint32_t pl_all[NW][2][4][8];     // [token parity][pair][head] BF16 pairs
+  __shared__ __attribute__((aligned(16))) float red_all[NW][C::RED];
+  __shared__ __attribute__((aligned(16))) uint32_t pl_all[NW][2][4][8];  // [parity][pair][head]
   __shared__ float alpha_all[NW][8];
   __shared__ float mg_m[NW][8], mg_l[NW][8];
 
@@ -318,7 +321,10 @@ void decode_tiled_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, i * 1024, 0);
+      // The whole byte offset goes in the vector offset: only the vector and
+      // instruction offsets are range-checked against num_records, the
+      // scalar offset is not.
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + i * 1024, 0, 0);
       kt[i].w[0] = x[0];
       kt[i].w[1] = x[1];
       kt[i].w[2] = x[2];
