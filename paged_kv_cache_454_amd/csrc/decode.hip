@@ -277,6 +277,7 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = rows * p.num_kv_heads * parts;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return fail(PA_EUNSUPPORTED, "decode: grid of %lld workgroups", (long long)grid);
+  if (launch_decode_persistent(p, stream)) return check_launch("decode");
   if (launch_decode_tiled(p, (unsigned)grid, stream)) return check_launch("decode");
   if (p.kv_bf16)
     launch_generic_d<bf16_t>(p, group, (unsigned)grid, stream);

@@ -46,6 +46,11 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream);
 // rows only). Returns false when the shape is not covered.
 bool launch_decode_tiled(const DecodeParams &p, unsigned grid, hipStream_t stream);
 
+// Persistent variant of the same shape class (single pass or partitioned):
+// one 8-wave workgroup per compute unit streaming a list of units. Returns
+// false when the shape is not covered.
+bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream);
+
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
