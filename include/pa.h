@@ -164,6 +164,8 @@ pa_status pa_decode_partitioned(float *part_out, float *part_max, float *part_su
  *  out          [device] out_dtype [num_seqs][num_q_heads][head_dim]
  *  part_*       [device] as written by pa_decode_partitioned
  *  context_lens [device] int32 [num_seqs]; 0 gives an all-zero row.
+ * A sequence whose context needs more than max_parts partitions gets a NaN
+ * row. max_parts <= 1024 (PA_EUNSUPPORTED otherwise).
  */
 pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
                     const float *part_sum, const int32_t *context_lens, int32_t num_seqs,

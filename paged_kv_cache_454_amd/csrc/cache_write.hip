@@ -43,14 +43,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t in_tok = u - tok * units_per_token;
     const int64_t head = in_tok / units_per_row;
     const int64_t piece = in_tok - head * units_per_row;
+    // The rows are read before the slot is checked (they are always in
+    // bounds), so the three loads are in flight together.
+    const int64_t src = u * UNIT;
+    const T kx = *reinterpret_cast<const T *>(key + src);
+    const T vx = *reinterpret_cast<const T *>(value + src);
     const int64_t slot = slot_mapping[tok];
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / block_size;
     const int64_t off = slot - blk * block_size;
-    const int64_t src = u * UNIT;
     const int64_t dst = ((blk * num_kv_heads + head) * block_size + off) * row_bytes + piece * UNIT;
-    *reinterpret_cast<T *>(key_cache + dst) = *reinterpret_cast<const T *>(key + src);
-    *reinterpret_cast<T *>(value_cache + dst) = *reinterpret_cast<const T *>(value + src);
+    *reinterpret_cast<T *>(key_cache + dst) = kx;
+    *reinterpret_cast<T *>(value_cache + dst) = vx;
   }
 }
 
