@@ -79,4 +79,8 @@ struct PrefillParams {
 
 pa_status launch_prefill(const PrefillParams &p, hipStream_t stream);
 
+// Matrix-core prefill for BF16, head_dim 256; false when the shape is not
+// covered.
+bool launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
+
 }  // namespace pa

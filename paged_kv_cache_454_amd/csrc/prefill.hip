@@ -1,14 +1,17 @@
 // Chunked paged prefill launcher.
 //
-// Correctness path: each packed query row of a sequence's chunk is a decode
-// over the prefix of that sequence up to and including the row's own
-// position (causal), run by the generic paged decode kernel.
+// BF16 caches with head_dim 256 run on the matrix-core kernel
+// (prefill_mfma.hip). Other shapes take the general path: each packed query
+// row of a sequence's chunk is a decode over the prefix of that sequence up
+// to and including the row's own position (causal), run by the generic
+// paged decode kernel.
 #include "launch.h"
 #include "pa_device.h"
 
 namespace pa {
 
 pa_status launch_prefill(const PrefillParams &p, hipStream_t stream) {
+  if (launch_prefill_mfma(p, stream)) return check_launch("pa_prefill_chunk");
   DecodeParams d{};
   d.query = p.query;
   d.key_cache = p.key_cache;

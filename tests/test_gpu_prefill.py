@@ -57,3 +57,62 @@ def test_prefill_full_size_sampled_rows():
     idx = sorted(rows)
     assert G.max_err(got[idx], want[idx]) <= G.BF16_TOL
     assert np.isfinite(got).all()
+
+
+def _oracle(case):
+    kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
+                                case.slot_mapping, case.block_size)
+    return oracle.prefill(case.query, kc, vc, case.block_tables, case.query_start_loc,
+                          case.context_lens, case.block_size, case.scale)
+
+
+# head_dim 256 BF16 runs on the matrix-core kernel: 128-row tiles over
+# (position, query head) pairs, 32-token K/V tiles, ragged chunk ends.
+@pytest.mark.parametrize("existing,chunks,hq,hkv,bs", [
+    ([0, 37, 1000], [130, 1, 77], 24, 4, 16),
+    ([5, 300], [512, 64], 8, 1, 32),
+    ([33], [200], 16, 2, 16),
+    ([100, 0], [40, 129], 4, 4, 16),
+    ([17, 2], [3, 30], 6, 2, 16),
+])
+def test_mfma_prefill_shapes(existing, chunks, hq, hkv, bs):
+    print(f"[prefill-mfma] existing={existing} chunks={chunks} hq={hq} hkv={hkv} bs={bs}",
+          flush=True)
+    case = inputs.prefill_case(existing, chunks, hq, hkv, 256, bs, seed=sum(existing) + 3)
+    t = G.to_dev(case)
+    G.write(t)
+    want = _oracle(case)
+    assert G.max_err(G.host(_run(case, t)), want) <= G.BF16_TOL
+    # BF16 output: within the tolerance plus half a BF16 ulp of the value
+    got = G.host(_run(case, t, out_dtype=torch.bfloat16))
+    assert (np.abs(got - want) <= G.BF16_TOL + np.abs(want) * 2.0 ** -8).all()
+
+
+def test_mfma_prefill_deterministic_and_permutation_invariant():
+    case = inputs.prefill_case([700, 64], [300, 200], 24, 4, 256, 16, pool_factor=1.5, seed=12)
+    t = G.to_dev(case)
+    G.write(t)
+    a = G.bits(_run(case, t))
+    assert np.array_equal(a, G.bits(_run(case, t)))
+    perm = torch.from_numpy(np.random.default_rng(2).permutation(case.num_blocks)).to(G.DEV)
+    inv = torch.argsort(perm)
+    t2 = dict(t)
+    t2["key_cache"] = t["key_cache"][inv].contiguous()
+    t2["value_cache"] = t["value_cache"][inv].contiguous()
+    bt = t["block_tables"].long()
+    t2["block_tables"] = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
+    assert np.array_equal(a, G.bits(_run(case, t2)))
+
+
+def test_mfma_prefill_invalid_block_poisons_only_rows_that_read_it():
+    case = inputs.prefill_case([40, 40], [40, 40], 12, 2, 256, 16, seed=13)
+    t = G.to_dev(case)
+    G.write(t)
+    good = G.host(_run(case, t))
+    bt = t["block_tables"].clone()
+    bt[0, 3] = case.num_blocks + 7     # tokens 48..63 of sequence 0
+    out = G.host(_run(case, dict(t, block_tables=bt)))
+    # sequence 0: queries at positions 40..79; those at >= 48 read block 3
+    assert np.array_equal(out[:8], good[:8])
+    assert np.isnan(out[8:40]).all()
+    assert np.array_equal(out[40:], good[40:])
