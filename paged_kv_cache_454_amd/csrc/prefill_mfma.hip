@@ -9,8 +9,8 @@
 // heads that share a KV head sit in the same tile and every K/V byte staged
 // in LDS serves all of them. A workgroup owns 128 rows (4 wavefronts x 32).
 //
-// Per 32-token K/V tile (K and V gathered through the block table into LDS,
-// double-buffered, the next tile's global loads in flight during compute):
+// Per 32-token K/V tile (K and V gathered through the block table straight
+// into an LDS ring of 4 tiles by buffer-to-LDS loads, 3 tiles in flight):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32
 //    rows, K = 16 channels; 16 steps over head_dim). In the accumulator
 //    layout each lane holds one query row (lane % 32) and 16 of the tile's
@@ -21,9 +21,10 @@
 //    rounded to BF16.
 //  * O^T += V^T . P^T with the same instruction (M = 32 channels, N = 32
 //    rows, K = 16 tokens): the weights are already in B-operand order in the
-//    lane that computed them; V is staged transposed in LDS ([channel][token])
-//    so the A operand is two 8-byte LDS reads. The k order of the tokens in
-//    both operands is the same permutation, which a sum over tokens ignores.
+//    lane that computed them; the A operand is read from the row-major V
+//    tile with two ds_read_b64_tr_b16 (transposing 4x4 blocks of 16-bit
+//    elements across lanes). The k order of the tokens in both operands is
+//    the same permutation, which a sum over tokens ignores.
 // Causality: query j of a chunk of n sits at position T - n + j and sees
 // tokens [0, T - n + j]; a workgroup stops at the last tile its rows can see.
 #include <math.h>
@@ -38,10 +39,7 @@ constexpr int D = 256;
 constexpr int WAVES = 4;
 constexpr int ROWS = WAVES * 32;        // query rows per workgroup
 constexpr int KT = 32;                  // tokens per K/V tile
-constexpr int KPITCH = D * 2 + 16;      // bytes per token row of the K tile (+16: bank spread)
-constexpr int VPITCH = KT * 2 + 8;      // bytes per channel row of the transposed V tile
-constexpr int KBYTES = KT * KPITCH;     // 16,896
-constexpr int VBYTES = D * VPITCH;      // 18,432
+constexpr int STAGES = 4;               // K/V tiles in the LDS ring (3 in flight)
 constexpr int MAX_TABLE = 2048;         // block ids staged in LDS
 constexpr float kLazy = 8.f;
 
@@ -61,6 +59,28 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// s_waitcnt immediates: vmcnt(n) with the other counters left at their maxima.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kVmcnt16 = waitcnt_vm(16);
+constexpr int kVmcnt8 = waitcnt_vm(8);
+constexpr int kVmcnt0 = waitcnt_vm(0);
+
+// XOR swizzles of the 16-byte chunk index within a 512-byte token row. K is
+// read by 32 lanes at 32 different tokens and one chunk; V (transpose reads)
+// by 8 tokens x 4 chunks per instruction. Both spread over the LDS banks.
+__device__ __forceinline__ int kswz(int tok) { return tok & 31; }
+__device__ __forceinline__ int vswz(int tok) { return (tok & 7) << 2; }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.
+__device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_v4 *)((__attribute__((address_space(3))) uint8_t *)lds_byte_ptr));
+  return __builtin_bit_cast(uint64_t, v);
+}
+
 __device__ __forceinline__ float other_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
@@ -74,12 +94,12 @@ __device__ __forceinline__ float other_half_sum(float x) {
 
 template <int G>
 __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams p, int row_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][KBYTES + VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGES][2][KT * D * 2];  // [K|V][token][ch]
   __shared__ int tab[MAX_TABLE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform (LDS DMA addresses)
   const int half = lane >> 5;  // which 8 of a 16-wide k step this lane supplies
   const int l32 = lane & 31;
 
@@ -142,59 +162,40 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
   const uint16_t *kpool = reinterpret_cast<const uint16_t *>(p.key_cache) + kvh * head_stride;
   const uint16_t *vpool = reinterpret_cast<const uint16_t *>(p.value_cache) + kvh * head_stride;
 
-  // Global -> register staging of one tile: K as 4 pieces of 16 B per thread
-  // (32 threads per token row), V as 2 token pairs x 16 B per thread.
-  // Tokens past the context, or in a block with an invalid id, read as zero.
-  vec16 kreg[4], vreg[2][2];
-  auto tok_ptr = [&](const uint16_t *pool, int tok) -> const uint16_t * {
-    if (tok >= wg_limit) return nullptr;
-    const int blk = tab[tok / bs];
-    if (blk < 0 || blk >= nb) return nullptr;
-    return pool + (int64_t)blk * block_stride + (int64_t)(tok % bs) * D;
-  };
-  auto fetch = [&](int it) {
-    const int t0 = it * KT;
+  // Tile staging: buffer-to-LDS loads, 1 KiB (two token rows) per wavefront
+  // instruction, four K and four V instructions per wavefront per tile. The
+  // resource of each instruction covers just the valid rows of its token pair
+  // (zero bytes past the context or for an invalid block id), so the LDS
+  // receives zeros there without a memory access. Chunks are XOR-swizzled
+  // (see kswz / vswz) for conflict-free operand reads.
+  auto issue_tile = [&](int it, int st) {
+    const int t_base = it * KT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int piece = tid + i * WAVES * 64;  // 32 tokens x 32 chunks
-      const int tok = piece >> 5, ch = piece & 31;
-      const uint16_t *src = tok_ptr(kpool, t0 + tok);
-      kreg[i] = src ? load16(src + ch * 8) : vec16{{0, 0, 0, 0}};
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + i * WAVES * 64;  // 16 token pairs x 32 chunks
-      const int pr = q >> 5, ch = q & 31;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint16_t *src = tok_ptr(vpool, t0 + 2 * pr + u);
-        vreg[i][u] = src ? load16(src + ch * 8) : vec16{{0, 0, 0, 0}};
+      const int pi = wave * 4 + i;        // token pair of the tile, 0..15
+      const int tok0 = t_base + 2 * pi;
+      int nv = wg_limit - tok0;
+      nv = __builtin_amdgcn_readfirstlane(nv < 0 ? 0 : (nv > 2 ? 2 : nv));
+      int blk = nv > 0 ? tab[tok0 / bs] : 0;
+      blk = __builtin_amdgcn_readfirstlane(blk);
+      if (blk < 0 || blk >= nb) {
+        nv = 0;
+        blk = 0;
       }
-    }
-  };
-  auto stash = [&](int buf) {
-    uint8_t *kl = kv_lds[buf];
-    uint8_t *vl = kv_lds[buf] + KBYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int piece = tid + i * WAVES * 64;
-      const int tok = piece >> 5, ch = piece & 31;
-      *reinterpret_cast<uint4 *>(kl + tok * KPITCH + ch * 16) =
-          make_uint4(kreg[i].w[0], kreg[i].w[1], kreg[i].w[2], kreg[i].w[3]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + i * WAVES * 64;
-      const int pr = q >> 5, ch = q & 31;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = vreg[i][0].w[w], b = vreg[i][1].w[w];
-        // channels 8ch + 2w and 8ch + 2w + 1, tokens 2pr and 2pr + 1
-        const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(vl + (8 * ch + 2 * w) * VPITCH + pr * 4) = lo;
-        *reinterpret_cast<uint32_t *>(vl + (8 * ch + 2 * w + 1) * VPITCH + pr * 4) = hi;
-      }
+      const int64_t off = (int64_t)blk * block_stride + (int64_t)(tok0 % bs) * D;
+      const int trow = 2 * pi + (lane >> 5);  // token row within the tile
+      const int ck = (lane & 31) ^ kswz(trow);
+      const int cv = (lane & 31) ^ vswz(trow);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(kpool + off), (short)0, nv * D * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(vpool + off), (short)0, nv * D * 2, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void *)(&stage[st][0][pi * 1024]), 16,
+          (lane >> 5) * 512 + ck * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void *)(&stage[st][1][pi * 1024]), 16,
+          (lane >> 5) * 512 + cv * 16, 0, 0, 0);
     }
   };
 
@@ -206,25 +207,42 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
   float m = kNoMax, l = 0.f;
   const float sl2 = p.scale * kLog2e;
 
-  if (ntiles > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
+  // Lane roles in the transpose reads of V (A operand of O^T): the lane is
+  // k = lane % 16 of a 16-lane group; it supplies the address of token
+  // row tok(k / 4) at channels 4 * (k % 4) of the group's 16-channel slice.
+  const int grp = lane >> 4, kq = lane & 15;
+  const int vd0 = 16 * (grp & 1) + 4 * (kq & 3);  // channel within the 32-channel tile
+  const int vtok = 4 * half + (kq >> 2);          // token offset (+16c, +8)
+
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < ntiles) issue_tile(t, t);
+
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) fetch(it + 1);  // in flight during this tile's math
-    const uint8_t *kl = kv_lds[buf];
-    const uint8_t *vl = kv_lds[buf] + KBYTES;
+    const int st = it % STAGES;
+    // This wave's loads for tile it are complete once at most the later
+    // tiles' (8 instructions each) are outstanding.
+    const int later = min(ntiles - 1 - it, STAGES - 2);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(kVmcnt16);
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(kVmcnt8);
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
+    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
+    const uint8_t *kl = stage[st][0];
+    const uint8_t *vl = stage[st][1];
     const int t0 = it * KT;
 
     // S^T (32 tokens x 32 rows), two independent accumulation chains.
     f32x16 s0 = {}, s1 = {};
+    const uint8_t *krow = kl + l32 * 512;
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
-      const uint4 ka = *reinterpret_cast<const uint4 *>(kl + l32 * KPITCH + (16 * k + 8 * half) * 2);
+      const uint4 ka = *reinterpret_cast<const uint4 *>(krow + (((2 * k + half) ^ kswz(l32)) * 16));
       const uint4 kb =
-          *reinterpret_cast<const uint4 *>(kl + l32 * KPITCH + (16 * (k + 1) + 8 * half) * 2);
+          *reinterpret_cast<const uint4 *>(krow + (((2 * k + 2 + half) ^ kswz(l32)) * 16));
       s0 = mfma(ka, qf[k], s0);
       s1 = mfma(kb, qf[k + 1], s1);
     }
@@ -249,7 +267,8 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
         for (int e = 0; e < 16; ++e) o[dt][e] *= a;
       m = mn;
     }
-    // Weights as the B operand of O^T: chunk c takes elements 8c .. 8c+7.
+    // Weights as the B operand of O^T: chunk c takes elements 8c .. 8c+7,
+    // i.e. tokens 16c + 4*half + (0..3) and 16c + 8 + 4*half + (0..3).
     uint4 pw[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -263,20 +282,23 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
       }
       pw[c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
-    // O^T (32 channels x 32 rows per dt) += V^T . P^T; the A operand's token
-    // order matches the weights': 16c + 8*(e/4) + 4*half + e%4.
+    // O^T (32 channels x 32 rows per dt) += V^T . P^T. The A operand comes
+    // from the row-major V tile through two transpose reads whose token
+    // order matches the weights'.
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint8_t *vrow = vl + (32 * dt + l32) * VPITCH;
+      const int d = 32 * dt + vd0;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (16 * c + 4 * half) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (16 * c + 8 + 4 * half) * 2);
-        o[dt] = mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), pw[c], o[dt]);
+        const int ta = 16 * c + vtok, tb = ta + 8;
+        const uint8_t *pa_ = vl + ta * 512 + (((d >> 3) ^ vswz(ta)) * 16) + (d & 7) * 2;
+        const uint8_t *pb_ = vl + tb * 512 + (((d >> 3) ^ vswz(tb)) * 16) + (d & 7) * 2;
+        const uint64_t va = tr_read(pa_), vb = tr_read(pb_);
+        const uint4 a = make_uint4((uint32_t)va, (uint32_t)(va >> 32), (uint32_t)vb,
+                                   (uint32_t)(vb >> 32));
+        o[dt] = mfma(a, pw[c], o[dt]);
       }
     }
-    if (it + 1 < ntiles) stash(buf ^ 1);
-    __syncthreads();
   }
 
   const float lt = other_half_sum(l);  // both halves of a row share row_ok
