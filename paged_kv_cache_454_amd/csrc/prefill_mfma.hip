@@ -7,10 +7,12 @@
 // Rows. The query rows of one KV head are the (position j, query head hh)
 // pairs of a sequence's chunk, flattened as r = j * G + hh, so the G query
 // heads that share a KV head sit in the same tile and every K/V byte staged
-// in LDS serves all of them. A workgroup owns 128 rows (4 wavefronts x 32).
+// in LDS serves all of them. A workgroup owns 256 rows (8 wavefronts x 32,
+// two per SIMD).
 //
 // Per 32-token K/V tile (K and V gathered through the block table straight
-// into an LDS ring of 4 tiles by buffer-to-LDS loads, 3 tiles in flight):
+// into an LDS ring of 4 tiles by buffer-to-LDS loads, 3 tiles in flight,
+// token pairs 1 KiB + 16 B apart):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32
 //    rows, K = 16 channels; 16 steps over head_dim). In the accumulator
 //    layout each lane holds one query row (lane % 32) and 16 of the tile's
@@ -36,10 +38,12 @@ namespace pa {
 namespace {
 
 constexpr int D = 256;
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;                // two per SIMD
 constexpr int ROWS = WAVES * 32;        // query rows per workgroup
 constexpr int KT = 32;                  // tokens per K/V tile
 constexpr int STAGES = 4;               // K/V tiles in the LDS ring (3 in flight)
+constexpr int PAIR = 1040;              // bytes per token pair in LDS: 2 x 512 + 16 of bank offset
+constexpr int TILE_BYTES = (KT / 2) * PAIR;  // one K (or V) tile
 constexpr int MAX_TABLE = 2048;         // block ids staged in LDS
 constexpr float kLazy = 8.f;
 
@@ -61,15 +65,15 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 
 // s_waitcnt immediates: vmcnt(n) with the other counters left at their maxima.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kVmcnt16 = waitcnt_vm(16);
 constexpr int kVmcnt8 = waitcnt_vm(8);
+constexpr int kVmcnt4 = waitcnt_vm(4);
 constexpr int kVmcnt0 = waitcnt_vm(0);
 
-// XOR swizzles of the 16-byte chunk index within a 512-byte token row. K is
-// read by 32 lanes at 32 different tokens and one chunk; V (transpose reads)
-// by 8 tokens x 4 chunks per instruction. Both spread over the LDS banks.
-__device__ __forceinline__ int kswz(int tok) { return tok & 31; }
-__device__ __forceinline__ int vswz(int tok) { return (tok & 7) << 2; }
+// LDS byte offset of channel ch of token row t in a K or V tile: token pairs
+// are 1 KiB apart plus 16 bytes, so the 32 token rows of an operand read fall
+// on distinct bank groups (two rows per group, the minimum for 512 bytes) and
+// every fragment address is a lane base plus an immediate.
+__device__ __forceinline__ int tile_off(int t, int ch) { return (t >> 1) * PAIR + (t & 1) * 512 + ch * 2; }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // (i % 4) of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.
@@ -93,8 +97,8 @@ __device__ __forceinline__ float other_half_sum(float x) {
 }
 
 template <int G>
-__global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams p, int row_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGES][2][KT * D * 2];  // [K|V][token][ch]
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p, int row_blocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGES][2][TILE_BYTES];  // [K|V][token pair]
   __shared__ int tab[MAX_TABLE];
 
   const int tid = threadIdx.x;
@@ -163,16 +167,15 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
   const uint16_t *vpool = reinterpret_cast<const uint16_t *>(p.value_cache) + kvh * head_stride;
 
   // Tile staging: buffer-to-LDS loads, 1 KiB (two token rows) per wavefront
-  // instruction, four K and four V instructions per wavefront per tile. The
+  // instruction, two K and two V instructions per wavefront per tile. The
   // resource of each instruction covers just the valid rows of its token pair
   // (zero bytes past the context or for an invalid block id), so the LDS
-  // receives zeros there without a memory access. Chunks are XOR-swizzled
-  // (see kswz / vswz) for conflict-free operand reads.
+  // receives zeros there without a memory access.
   auto issue_tile = [&](int it, int st) {
     const int t_base = it * KT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pi = wave * 4 + i;        // token pair of the tile, 0..15
+    for (int i = 0; i < KT / 2 / WAVES; ++i) {
+      const int pi = wave * (KT / 2 / WAVES) + i;  // token pair of the tile, 0..15
       const int tok0 = t_base + 2 * pi;
       int nv = wg_limit - tok0;
       nv = __builtin_amdgcn_readfirstlane(nv < 0 ? 0 : (nv > 2 ? 2 : nv));
@@ -183,19 +186,16 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
         blk = 0;
       }
       const int64_t off = (int64_t)blk * block_stride + (int64_t)(tok0 % bs) * D;
-      const int trow = 2 * pi + (lane >> 5);  // token row within the tile
-      const int ck = (lane & 31) ^ kswz(trow);
-      const int cv = (lane & 31) ^ vswz(trow);
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t *>(kpool + off), (short)0, nv * D * 2, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t *>(vpool + off), (short)0, nv * D * 2, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void *)(&stage[st][0][pi * 1024]), 16,
-          (lane >> 5) * 512 + ck * 16, 0, 0, 0);
+          rk, (__attribute__((address_space(3))) void *)(&stage[st][0][pi * PAIR]), 16, lane * 16,
+          0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(&stage[st][1][pi * 1024]), 16,
-          (lane >> 5) * 512 + cv * 16, 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void *)(&stage[st][1][pi * PAIR]), 16, lane * 16,
+          0, 0, 0);
     }
   };
 
@@ -221,12 +221,13 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
   for (int it = 0; it < ntiles; ++it) {
     const int st = it % STAGES;
     // This wave's loads for tile it are complete once at most the later
-    // tiles' (8 instructions each) are outstanding.
+    // tiles' are outstanding
+    // (4 instructions per tile per wave)
     const int later = min(ntiles - 1 - it, STAGES - 2);
     if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(kVmcnt16);
-    else if (later == 1)
       __builtin_amdgcn_s_waitcnt(kVmcnt8);
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(kVmcnt4);
     else
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
@@ -235,24 +236,18 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
     const uint8_t *vl = stage[st][1];
     const int t0 = it * KT;
 
-    // S^T (32 tokens x 32 rows), two independent accumulation chains.
-    f32x16 s0 = {}, s1 = {};
-    const uint8_t *krow = kl + l32 * 512;
+    // S^T (32 tokens x 32 rows).
+    f32x16 s0 = {};
+    const uint8_t *krow = kl + tile_off(l32, 8 * half);
 #pragma unroll
-    for (int k = 0; k < 16; k += 2) {
-      const uint4 ka = *reinterpret_cast<const uint4 *>(krow + (((2 * k + half) ^ kswz(l32)) * 16));
-      const uint4 kb =
-          *reinterpret_cast<const uint4 *>(krow + (((2 * k + 2 + half) ^ kswz(l32)) * 16));
-      s0 = mfma(ka, qf[k], s0);
-      s1 = mfma(kb, qf[k + 1], s1);
-    }
+    for (int k = 0; k < 16; ++k) s0 = mfma(*reinterpret_cast<const uint4 *>(krow + 32 * k), qf[k], s0);
     // Element e of the accumulator is token 8*(e/4) + 4*half + e%4.
     float z[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int tok = t0 + 8 * (e >> 2) + 4 * half + (e & 3);
-      const float v = (s0[e] + s1[e]) * sl2;
+      const float v = s0[e] * sl2;
       z[e] = tok < limit ? v : -INFINITY;
       mx = fmaxf(mx, z[e]);
     }
@@ -285,15 +280,14 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_mfma_kernel(PrefillParams 
     // O^T (32 channels x 32 rows per dt) += V^T . P^T. The A operand comes
     // from the row-major V tile through two transpose reads whose token
     // order matches the weights'.
+    const uint8_t *vbase = vl + tile_off(vtok, vd0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = 32 * dt + vd0;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int ta = 16 * c + vtok, tb = ta + 8;
-        const uint8_t *pa_ = vl + ta * 512 + (((d >> 3) ^ vswz(ta)) * 16) + (d & 7) * 2;
-        const uint8_t *pb_ = vl + tb * 512 + (((d >> 3) ^ vswz(tb)) * 16) + (d & 7) * 2;
-        const uint64_t va = tr_read(pa_), vb = tr_read(pb_);
+        // tokens 16c + vtok and 16c + 8 + vtok: 8 and 4 token pairs further
+        const uint64_t va = tr_read(vbase + c * 8 * PAIR + dt * 64);
+        const uint64_t vb = tr_read(vbase + c * 8 * PAIR + 4 * PAIR + dt * 64);
         const uint4 a = make_uint4((uint32_t)va, (uint32_t)(va >> 32), (uint32_t)vb,
                                    (uint32_t)(vb >> 32));
         o[dt] = mfma(a, pw[c], o[dt]);
