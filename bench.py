@@ -16,16 +16,31 @@ step (exact context tokens x 4096 B per token per layer / step time); also
 tokens/s (64 new tokens per step), the decode kernel's roofline against
 8 TB/s HBM (its own launches timed with HIP events on the launch stream) and
 the CPU oracle timed on a bounded sample of the same workload.
+
+After the decode measurement, a separate leg times the chunked-prefill
+workload (16 sequences with 0-6000 cached tokens, a 512-token causal chunk
+each, 24/4 heads, head_dim 256, BF16, block_size 16): the slot write of the
+chunk's K/V and pa_prefill_chunk, the latter against the BF16 matrix-core
+peak. It reports under "prefill" and does not enter `value`.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix cores, vendor figure
+HERE = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per decode launch, measured with FETCH_SIZE / WRITE_SIZE counters
+# and scaled by the same counters' reading for a plain copy of known size.
+TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_persistent_mixed_64seq_hbm_counters.md")
+TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
+                   for f in ("decode_persistent.hip", "pa_device.h")]
 WORKLOAD_NAMES = {
     "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
     "long": "long-context split decode, 4 seqs {8192, 16384, 32768, 32768}, bs 32",
@@ -42,8 +57,14 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=512)
     ap.add_argument("--workload", default="mixed", choices=["mixed", "long", "uniform"],
                     help="decode workload (default: the mixed-length 16-layer batch)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 256 MiB device copy three times: its "
+                         "FETCH_SIZE/WRITE_SIZE under a counter profiler give the scale "
+                         "between those counters and bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
+    ap.add_argument("--prefill-reps", type=int, default=10,
+                    help="timed repetitions of the chunked-prefill leg (0 skips it)")
     return ap.parse_args()
 
 
@@ -78,6 +99,87 @@ def cpu_baseline(seed, budget_s):
                       f"fp64 decode of all {case.num_seqs} sequences, {done_tokens} context "
                       f"tokens in total) in {dt:.1f} s; decode tokens/s for a 16-layer step "
                       f"{done_seqs / dt / 16:.3f}"}
+
+
+def counted_traffic(workload, partition_size, seed):
+    """The counter record's HBM bytes per decode launch, or None when the record
+    was taken on another workload or the kernel's source has changed since."""
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    except (OSError, AttributeError, ValueError):
+        return None
+    if (rec.get("source_sha256") != h.hexdigest() or rec.get("workload") != workload
+            or rec.get("partition_size") != partition_size or rec.get("seed") != seed):
+        return None
+    return int(rec["traffic_bytes"])
+
+
+def timed_launches(fn, reps, stream):
+    """Mean duration (ms) of fn's launch, each bracketed by HIP events on the
+    stream it runs on."""
+    import torch
+    pairs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+
+def prefill_leg(seed, reps, dev):
+    """Chunked prefill at full size: the chunk's slot write and the causal
+    paged attention of its 8,192 query rows."""
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    from paged_kv_cache_454_amd import inputs
+    t, m = inputs.device_prefill_case(seed, dev)
+    stream = torch.cuda.current_stream()
+    out = torch.empty(tuple(t["query"].shape), dtype=torch.float32, device=dev)
+
+    def write():
+        pa.pa_reshape_and_cache(t["key"], t["value"], t["key_cache"], t["value_cache"],
+                                t["slot_mapping"], stream=stream)
+
+    def prefill():
+        pa.pa_prefill_chunk(out, t["query"], t["key_cache"], t["value_cache"],
+                            t["block_tables"], t["query_start_loc"], t["context_lens"],
+                            m["max_query_len"], m["scale"], stream=stream)
+
+    write()
+    prefill()
+    torch.cuda.synchronize()
+    w_ms = timed_launches(write, reps, stream)
+    p_ms = timed_launches(prefill, reps, stream)
+    hq, d = t["query"].shape[1], t["query"].shape[2]
+    hkv = t["key"].shape[1]
+    n = m["chunk"]
+    # Q.K^T and P.V over the causal span: query j of sequence s sees c_s + j + 1 keys.
+    flops = sum(4 * d * hq * (n * int(c) + n * (n + 1) // 2) for c in m["existing"])
+    kv_bytes = int(m["lens"].sum()) * hkv * d * 2 * 2
+    w_bytes = 2 * 2 * t["key"].numel() * 2   # K and V rows, read and written, BF16
+    tf = flops / (p_ms * 1e-3) / 1e12
+    return {
+        "workload": "chunked prefill, 16 seqs x (0-6000 cached + 512-token causal chunk), "
+                    "24/4 heads, d 256, bs 16, 1 layer",
+        "query_rows": int(t["query"].shape[0]), "flops": flops,
+        "prefill_us": round(p_ms * 1e3, 2), "tflops": round(tf, 1),
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_chunk", "achieved": round(tf, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "kv_context_bytes": kv_bytes,
+        "write_us": round(w_ms * 1e3, 2),
+        "write_gbs": round(w_bytes / (w_ms * 1e-3) / 1e9, 1),
+        "reps": reps,
+    }
 
 
 def main():
@@ -177,12 +279,23 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic(W, P, args.seed),
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
+    if args.prefill_reps > 0:
+        del layers, po, pm, ps, outs
+        torch.cuda.empty_cache()
+        result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
     if args.cpu_seconds > 0 and W == "mixed":
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result), flush=True)
 
 

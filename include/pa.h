@@ -189,8 +189,10 @@ pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
  *  max_query_len   host bound on n_s (sizes the launch grid); queries past
  *                  it are not computed
  * Supported: kv_dtype BF16, head_dim 256 or 128 or 64, num_q_heads /
- * num_kv_heads <= 8. Q.K^T and P.V run on the matrix cores (MFMA, fp32
- * accumulation).
+ * num_kv_heads <= 8. With head_dim 256, an even block_size and
+ * max_blocks_per_seq <= 2048, Q.K^T and P.V run on the matrix cores (MFMA,
+ * BF16 operands, fp32 accumulation, P rounded to BF16); other supported
+ * shapes run on the vector units with fp32 arithmetic.
  */
 pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                            const void *value_cache, const int32_t *block_tables,

@@ -322,10 +322,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
 }  // namespace
 
-// The MFMA path covers BF16, head_dim 256 and tables of up to 2048 blocks
-// per sequence; false otherwise.
+// The MFMA path covers BF16, head_dim 256, even block sizes (a token pair
+// never straddles two blocks) and tables of up to 2048 blocks per sequence;
+// false otherwise.
 bool launch_prefill_mfma(const PrefillParams &p, hipStream_t stream) {
-  if (p.head_dim != D || p.max_blocks_per_seq > MAX_TABLE) return false;
+  if (p.head_dim != D || p.block_size % 2 != 0 || p.max_blocks_per_seq > MAX_TABLE) return false;
   const int group = p.num_q_heads / p.num_kv_heads;
   const int64_t row_blocks = ((int64_t)p.max_query_len * group + ROWS - 1) / ROWS;
   const int64_t grid = row_blocks * p.num_seqs * p.num_kv_heads;

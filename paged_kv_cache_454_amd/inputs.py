@@ -337,3 +337,45 @@ def device_decode_layers(name, seed, layers, device, dtype=None):
         lens=lens, num_blocks=num_blocks, scale=p.get("scale") or 1.0 / math.sqrt(d),
         partition_size=p.get("partition_size", 512))
     return out, meta
+
+
+def device_prefill_case(seed, device):
+    """The full-size chunked-prefill workload generated on the device for
+    timing: the integer layout (seeded scatter of each sequence's blocks, the
+    slots of the chunk's positions c_s .. c_s + 511, the packed query offsets)
+    on the host, and the K/V pools, the chunk's new K/V and its queries drawn
+    N(0,1) on the device with a seeded torch generator and rounded to BF16."""
+    import torch
+    p = PRESETS["prefill"]
+    lens = preset_lengths("prefill", seed)
+    chunk, bs = p["chunk"], p["block_size"]
+    ex = lens - chunk
+    rng = np.random.default_rng(seed)
+    bps = [_ceil_div(int(t), bs) for t in lens]
+    num_blocks = max(1, sum(bps))
+    tables = _scatter_tables(rng, bps, num_blocks)
+    n_new = int(chunk * len(lens))
+    slots = np.empty(n_new, dtype=np.int64)
+    i = 0
+    for s in range(len(lens)):
+        pos = np.arange(int(ex[s]), int(lens[s]))
+        slots[i:i + len(pos)] = tables[s, pos // bs].astype(np.int64) * bs + pos % bs
+        i += len(pos)
+    qsl = np.arange(len(lens) + 1, dtype=np.int32) * chunk
+    hq, hkv, d = p["num_q_heads"], p["num_kv_heads"], p["head_dim"]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = {}
+    for nm, shape in (("key_cache", (num_blocks, hkv, bs, d)),
+                      ("value_cache", (num_blocks, hkv, bs, d)),
+                      ("key", (n_new, hkv, d)), ("value", (n_new, hkv, d)),
+                      ("query", (n_new, hq, d))):
+        t[nm] = torch.randn(shape, generator=g, device=device,
+                            dtype=torch.float32).to(torch.bfloat16)
+    t.update(context_lens=torch.from_numpy(lens.astype(np.int32)).to(device),
+             block_tables=torch.from_numpy(tables).to(device),
+             slot_mapping=torch.from_numpy(slots).to(device),
+             query_start_loc=torch.from_numpy(qsl).to(device))
+    meta = dict(lens=lens, existing=ex, chunk=chunk, num_blocks=num_blocks,
+                scale=1.0 / math.sqrt(d), max_query_len=chunk)
+    return t, meta

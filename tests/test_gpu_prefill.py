@@ -66,14 +66,21 @@ def _oracle(case):
                           case.context_lens, case.block_size, case.scale)
 
 
-# head_dim 256 BF16 runs on the matrix-core kernel: 128-row tiles over
-# (position, query head) pairs, 32-token K/V tiles, ragged chunk ends.
+# head_dim 256 BF16 with an even block size runs on the matrix-core kernel:
+# 256-row tiles over (position, query head) pairs, 32-token K/V tiles staged
+# as token pairs, ragged chunk ends. Block sizes 2 and 6 put several blocks
+# (and, at 6, block boundaries that are not tile boundaries) in every tile;
+# an odd block size (a pair would straddle two blocks) takes the generic
+# kernel and must give the same results.
 @pytest.mark.parametrize("existing,chunks,hq,hkv,bs", [
     ([0, 37, 1000], [130, 1, 77], 24, 4, 16),
     ([5, 300], [512, 64], 8, 1, 32),
     ([33], [200], 16, 2, 16),
     ([100, 0], [40, 129], 4, 4, 16),
     ([17, 2], [3, 30], 6, 2, 16),
+    ([1, 20], [37, 9], 4, 1, 2),
+    ([10, 0], [65, 33], 8, 2, 6),
+    ([3, 50], [40, 70], 8, 2, 5),
 ])
 def test_mfma_prefill_shapes(existing, chunks, hq, hkv, bs):
     print(f"[prefill-mfma] existing={existing} chunks={chunks} hq={hq} hkv={hkv} bs={bs}",
