@@ -95,7 +95,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a) {
   return __builtin_bit_cast(uint32_t, v) & 0xffffu;
 }
 
-__device__ __forceinline__ int lane_of(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
 
 template <int G>
 struct Cfg {
@@ -131,24 +130,28 @@ struct SeqParts {
   int T, nfull, partial, bad;
 };
 
+// 32-bit arithmetic throughout: the host guarantees max_blocks_per_seq *
+// block_size < 2^31, so the clamped T fits.
 template <bool SPLIT>
 __device__ __forceinline__ SeqParts seq_parts(const DecodeParams &p, int s) {
   SeqParts r{0, 0, 0, 0};
   if (s >= p.num_seqs) return r;
-  int64_t T = p.context_lens[s];
+  int T = p.context_lens[s];
   T = T < 0 ? 0 : T;
-  const int64_t cap = (int64_t)p.max_blocks_per_seq * p.block_size;
+  const int cap = p.max_blocks_per_seq * p.block_size;
   if (T > cap) {
     r.bad = 1;
     T = cap;
   }
-  r.T = (int)T;
+  r.T = T;
   if (SPLIT) {
-    const int64_t P = p.partition_size;
-    if (T > (int64_t)p.max_parts * P) r.bad = 1;
-    int64_t np = (T + P - 1) / P;
-    if (np > p.max_parts) np = p.max_parts;
-    int64_t nf = T / P;
+    const unsigned P = (unsigned)p.partition_size;
+    unsigned nf = (unsigned)T / P;
+    unsigned np = nf + ((unsigned)T != nf * P);  // ceil(T / P)
+    if (np > (unsigned)p.max_parts) {
+      r.bad = 1;  // T > max_parts * P
+      np = (unsigned)p.max_parts;
+    }
     if (nf > np) nf = np;
     r.nfull = (int)nf;
     r.partial = np > nf;
@@ -157,6 +160,13 @@ __device__ __forceinline__ SeqParts seq_parts(const DecodeParams &p, int s) {
   }
   return r;
 }
+
+// The planner's lanes exchange values through LDS. A wavefront's LDS
+// operations execute in program order, but the compiler treats each lane as
+// a thread of its own and may move one lane's store past loads that only the
+// other lanes make (it has merged such a store into a later one). This
+// compiler barrier keeps every memory operation on its side.
+__device__ __forceinline__ void lane_exchange_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -187,7 +197,7 @@ __device__ __forceinline__ int upper_index(const int *incl, int off) {
 // workgroups in snake order (round k goes 0..grid-1 when k is even,
 // grid-1..0 when odd). Big units go first and the round-by-round reversal
 // evens out the loads; in single-pass mode every sequence is one partial
-// unit, so the longest contexts start first.
+// unit, so the longest contexts start first. Run by one wavefront.
 // scr: 192 ints of this wave's LDS (prologue scratch).
 template <bool SPLIT>
 __device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit, int &bad_part,
@@ -198,13 +208,17 @@ __device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit
   const int P = SPLIT ? p.partition_size : 0;
   int c_s = -1, c_h = 0, c_p = 0, c_T = 0, c_bad = 0;
 
-  // Full partitions, sequence-major.
+  // Full partitions, sequence-major. The first 64 sequences' counts are
+  // loaded once and serve the partial partitions below as well.
+  const SeqParts sp_first = seq_parts<SPLIT>(p, lane);
   int F = 0;
   for (int s0 = 0; s0 < S; s0 += 64) {
-    const SeqParts sp = seq_parts<SPLIT>(p, s0 + lane);
+    const SeqParts sp = s0 == 0 ? sp_first : seq_parts<SPLIT>(p, s0 + lane);
     const int incl = wave_incl_scan(sp.nfull * H, lane);
     const int tot = __shfl(incl, 63, 64);
+    lane_exchange_fence();
     scr[lane] = incl;
+    lane_exchange_fence();
     const int off = a - F;
     const bool hit = off >= 0 && off < tot;
     const int i = hit ? upper_index(scr, off) : lane;
@@ -223,14 +237,24 @@ __device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit
   // Last, partial partitions.
   int NPH = 0;  // partial units
   if (S <= 64) {
-    const SeqParts sp = seq_parts<SPLIT>(p, lane);
-    const int sz = sp.partial ? sp.T - sp.nfull * P : -1;
+    const SeqParts sp = sp_first;
+    // A unique key per sequence that orders by decreasing size, then by
+    // increasing sequence index; the rank is the count of larger keys.
+    // Every lane reads all 64 keys from LDS (broadcast reads, no serial
+    // dependency); lanes past S hold -1.
+    const int sz = sp.T - sp.nfull * P;
+    const int key = sp.partial ? (min(sz, (1 << 25) - 1) << 6) | (63 - lane) : -1;
+    scr[128 + lane] = key;
+    lane_exchange_fence();
     int rank = 0;
-    for (int j = 0; j < S; ++j) {
-      const int szj = __builtin_amdgcn_readlane(sz, j);
-      rank += (szj > sz) || (szj == sz && j < lane);
+#pragma unroll
+    for (int j = 0; j < 64; j += 4) {
+      const int4 k4 = *reinterpret_cast<const int4 *>(&scr[128 + j]);
+      rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
     }
+    lane_exchange_fence();
     if (sp.partial) scr[64 + rank] = lane;
+    lane_exchange_fence();
     const int nps = __popcll(__builtin_amdgcn_ballot_w64(sp.partial != 0));
     NPH = nps * H;
     const int off = a - F;
@@ -251,7 +275,9 @@ __device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit
       const SeqParts sp = seq_parts<SPLIT>(p, s0 + lane);
       const int incl = wave_incl_scan(sp.partial * H, lane);
       const int tot = __shfl(incl, 63, 64);
+      lane_exchange_fence();
       scr[lane] = incl;
+      lane_exchange_fence();
       const int off = a - F - NPH;
       const bool hit = off >= 0 && off < tot;
       const int i = hit ? upper_index(scr, off) : lane;
@@ -268,7 +294,8 @@ __device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit
     }
   }
 
-  active = c_s >= 0;
+  // Only a unit inside the batch is ever entered.
+  active = c_s >= 0 && c_s < S && c_h >= 0 && c_h < H && c_T >= 0;
   if (!active) {
     unit = make_int4(0, 0, 0, 0);
     bad_part = 0;
@@ -303,21 +330,29 @@ void decode_persistent_kernel(DecodeParams p) {
   uint32_t(*pl)[4][8] = pl_all[wave];
   uint16_t *pl16 = reinterpret_cast<uint16_t *>(pl_all[wave]);
 
-  // ---- The workgroup's candidate units, one per lane (same in every wave).
-  // Unit info lives in VGPR lanes for the prologue and in LDS afterwards.
+  // ---- The workgroup's units, planned by wave 0 and shared through LDS.
   __shared__ int4 uinfo[MAXU];  // (s, h, lo, hi)
   __shared__ int ubadpart[MAXU];  // part * 2 + bad
+  __shared__ uint32_t act_lds[2];
   const int S = p.num_seqs, H = p.num_kv_heads, HQ = p.num_q_heads;
   constexpr bool split = SPLIT;
-  int4 my{0, 0, 0, 0};
-  int my_bp = 0, my_act = 0;
-  plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
-  const uint64_t act_mask = __builtin_amdgcn_ballot_w64(my_act != 0);
-  if (act_mask == 0) return;  // uniform for the workgroup
   if (wave == 0) {
+    int4 my{0, 0, 0, 0};
+    int my_bp = 0, my_act = 0;
+    plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
     uinfo[lane] = my;
     ubadpart[lane] = my_bp;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(my_act != 0);
+    if (lane == 0) {
+      act_lds[0] = (uint32_t)m;
+      act_lds[1] = (uint32_t)(m >> 32);
+    }
   }
+  __syncthreads();  // the plan is visible to every wave
+  const uint64_t act_mask =
+      (uint64_t)__builtin_amdgcn_readfirstlane(act_lds[0]) |
+      ((uint64_t)__builtin_amdgcn_readfirstlane(act_lds[1]) << 32);
+  if (act_mask == 0) return;  // uniform for the workgroup
 
   const int bs = p.block_size;
   const int64_t head_stride = (int64_t)bs * D;
@@ -338,16 +373,11 @@ void decode_persistent_kernel(DecodeParams p) {
   const __amdgpu_buffer_rsrc_t sum_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(p.part_sum, (short)0, SPLIT ? (int)(rows * 4) : 0, 0x00020000);
 
-  // Unit j's (s, h, lo, hi): from the VGPR lanes before the first barrier,
-  // from LDS after it.
-  bool info_in_lds = false;
+  // Unit j's (s, h, lo, hi).
   auto info = [&](int j) -> int4 {
-    if (info_in_lds) {
-      const int4 v = uinfo[j];
-      return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                       __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
-    }
-    return make_int4(lane_of(my.x, j), lane_of(my.y, j), lane_of(my.z, j), lane_of(my.w, j));
+    const int4 v = uinfo[j];
+    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
   // A wave's tiles of a unit of nt tiles: kk = wave, wave + NW, ...; the
   // count is padded to even with empty tiles so that stream positions
@@ -475,7 +505,6 @@ void decode_persistent_kernel(DecodeParams p) {
   };
   stage_queries(act_mask);
   __syncthreads();
-  info_in_lds = true;
 
   const float sl2 = p.scale * kLog2e;
   float acc[G][8];
