@@ -457,8 +457,8 @@ void decode_persistent_kernel(DecodeParams p) {
     for (int i = 0; i < LOADS; ++i) {
       // Vector offset + immediate offset: both are range-checked against
       // num_records (the scalar offset would not be).
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(i < 4 ? r.lo : r.hi,
-                                                            lane_off + (i & 3) * 1024, 0, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+          i < 4 ? r.lo : r.hi, lane_off + (i & 3) * 1024, 0, kStreamLoad);
       kt[i].w[0] = x[0];
       kt[i].w[1] = x[1];
       kt[i].w[2] = x[2];

@@ -324,7 +324,7 @@ void decode_tiled_kernel(DecodeParams p) {
       // The whole byte offset goes in the vector offset: only the vector and
       // instruction offsets are range-checked against num_records, the
       // scalar offset is not.
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + i * 1024, 0, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + i * 1024, 0, kStreamLoad);
       kt[i].w[0] = x[0];
       kt[i].w[1] = x[1];
       kt[i].w[2] = x[2];

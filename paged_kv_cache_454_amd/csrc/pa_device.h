@@ -64,6 +64,12 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v, bool 
     reinterpret_cast<float *>(out)[idx] = v;
 }
 
+// Cache policy of the K/V tile loads: non-temporal (the nt bit of the
+// buffer instruction). Decode reads every cached K/V byte once per step, so
+// keeping it in L2 and the Infinity Cache only evicts useful lines; on
+// MI355X random 8 KiB gathers run measurably faster this way.
+constexpr int kStreamLoad = 2;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Finite stand-in for "no logit seen yet": exp2(kNoMax - m) is 0 for any
