@@ -765,6 +765,12 @@ bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream) {
   const int64_t units = parts * p.num_seqs * p.num_kv_heads;
   if (units <= 0 || units > 0x7fffffff) return false;
   int64_t grid = num_cus();
+  // Split mode takes the tiled kernel (a workgroup per unit, two per CU,
+  // balanced by the hardware dispatcher) when the persistent one cannot pay
+  // for its planner and ring: with at most one unit per CU, or with
+  // partitions under 2 tiles per wavefront, where padding every wavefront's
+  // share of a unit to an even count would leave half the ring empty.
+  if (p.partition_size > 0 && (units <= grid || p.partition_size < 2 * NW * TILE)) return false;
   if (grid > units) grid = units;
   if (grid * MAXU < units) return false;  // more than 64 units per workgroup
   const int64_t out_bytes = (int64_t)p.num_seqs * p.num_q_heads * parts * D *
