@@ -12,7 +12,8 @@
 //
 // Per 32-token K/V tile (K and V gathered through the block table straight
 // into an LDS ring of 4 tiles by buffer-to-LDS loads, 3 tiles in flight,
-// token pairs 1 KiB + 16 B apart):
+// token pairs 1 KiB + 16 B apart; one barrier per tile, after each wave's
+// own wait for its loads of that tile):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32
 //    rows, K = 16 channels; 16 steps over head_dim). In the accumulator
 //    layout each lane holds one query row (lane % 32) and 16 of the tile's
@@ -66,8 +67,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 // s_waitcnt immediates: vmcnt(n) with the other counters left at their maxima.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kVmcnt8 = waitcnt_vm(8);
-constexpr int kVmcnt4 = waitcnt_vm(4);
-constexpr int kVmcnt0 = waitcnt_vm(0);
 
 // LDS byte offset of channel ch of token row t in a K or V tile: token pairs
 // are 1 KiB apart plus 16 bytes, so the 32 token rows of an operand read fall
@@ -85,6 +84,34 @@ __device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
   return __builtin_bit_cast(uint64_t, v);
 }
 
+// One buffer-to-LDS load: each lane's 16 bytes at `voffset` of the buffer
+// go to LDS address lds_addr + 16 * lane. Issued through inline assembly so
+// that the compiler's wait-count pass does not track it: that pass cannot
+// tell the ring's stages apart and would wait for every outstanding load
+// before each LDS read. The kernel waits for these loads itself (vmcnt, then
+// a barrier) before any wave reads the stage they fill; vector memory
+// operations complete in order, so the compiler's own waits for other loads
+// stay correct (they only become stricter).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_load16(u32x4v rsrc, uint32_t lds_addr, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer resource over [base, base + bytes): raw buffer, no stride, the
+// same dword 3 as the rest of the library's resources.
+__device__ __forceinline__ u32x4v raw_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4v r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
 __device__ __forceinline__ float other_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
@@ -98,7 +125,13 @@ __device__ __forceinline__ float other_half_sum(float x) {
 
 template <int G>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(PrefillParams p, int row_blocks) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGES][2][TILE_BYTES];  // [K|V][token pair]
+  // The ring's stages are separate arrays and the loop below is unrolled by
+  // STAGES, so every buffer-to-LDS load and every LDS read names its stage
+  // statically: the compiler can then tell that the loads issued for tile
+  // it+3 do not write the stage being read, and does not wait for them.
+  typedef uint8_t Stage[2][TILE_BYTES];  // [K|V][token pair]
+  __shared__ __attribute__((aligned(16))) Stage stage0, stage1, stage2, stage3;
+  static_assert(STAGES == 4, "the ring is four named stages");
   __shared__ int tab[MAX_TABLE];
 
   const int tid = threadIdx.x;
@@ -171,7 +204,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // resource of each instruction covers just the valid rows of its token pair
   // (zero bytes past the context or for an invalid block id), so the LDS
   // receives zeros there without a memory access.
-  auto issue_tile = [&](int it, int st) {
+  auto issue_tile = [&](int it, Stage &dst) {
     const int t_base = it * KT;
 #pragma unroll
     for (int i = 0; i < KT / 2 / WAVES; ++i) {
@@ -186,16 +219,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         blk = 0;
       }
       const int64_t off = (int64_t)blk * block_stride + (int64_t)(tok0 % bs) * D;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(kpool + off), (short)0, nv * D * 2, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(vpool + off), (short)0, nv * D * 2, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void *)(&stage[st][0][pi * PAIR]), 16, lane * 16,
-          0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(&stage[st][1][pi * PAIR]), 16, lane * 16,
-          0, 0, 0);
+      const uint32_t kdst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)&dst[0][pi * PAIR])));
+      const uint32_t vdst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)&dst[1][pi * PAIR])));
+      lds_load16(raw_rsrc(kpool + off, nv * D * 2), kdst, lane * 16);
+      lds_load16(raw_rsrc(vpool + off, nv * D * 2), vdst, lane * 16);
     }
   };
 
@@ -214,26 +243,29 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int vd0 = 16 * (grp & 1) + 4 * (kq & 3);  // channel within the 32-channel tile
   const int vtok = 4 * half + (kq >> 2);          // token offset (+16c, +8)
 
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < ntiles) issue_tile(t, t);
+  // Tiles are issued unconditionally: one past the last needed token has an
+  // empty resource, so it reads nothing and fills a stage no one reads with
+  // zeros. Every step then issues the same 4 instructions per wave and the
+  // compiler's wait counts stay exact (a conditional issue would make it
+  // wait for every load before each LDS read).
+  // The query fragments must be in registers before the first tile loads
+  // leave: a wait for them inside the loop would also wait for every tile
+  // load in flight.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  issue_tile(0, stage0);
+  issue_tile(1, stage1);
+  issue_tile(2, stage2);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it % STAGES;
-    // This wave's loads for tile it are complete once at most the later
-    // tiles' are outstanding
-    // (4 instructions per tile per wave)
-    const int later = min(ntiles - 1 - it, STAGES - 2);
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(kVmcnt8);
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(kVmcnt4);
-    else
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  // One tile: `cur` holds tile it, `nxt` (the stage tile it-1 used) receives
+  // tile it+3.
+  auto step = [&](int it, Stage &cur, Stage &nxt) {
+    // This wave's loads for tile it are complete once only the two later
+    // tiles' are outstanding (4 instructions per tile per wave).
+    __builtin_amdgcn_s_waitcnt(kVmcnt8);
     __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
-    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
-    const uint8_t *kl = stage[st][0];
-    const uint8_t *vl = stage[st][1];
+    issue_tile(it + STAGES - 1, nxt);
+    const uint8_t *kl = cur[0];
+    const uint8_t *vl = cur[1];
     const int t0 = it * KT;
 
     // S^T (32 tokens x 32 rows).
@@ -293,7 +325,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         o[dt] = mfma(a, pw[c], o[dt]);
       }
     }
+  };
+
+  for (int it = 0; it < ntiles; it += STAGES) {
+    step(it, stage0, stage3);
+    if (it + 1 >= ntiles) break;
+    step(it + 1, stage1, stage0);
+    if (it + 2 >= ntiles) break;
+    step(it + 2, stage2, stage1);
+    if (it + 3 >= ntiles) break;
+    step(it + 3, stage3, stage2);
   }
+  // The loads issued for the three tiles past the end (empty, but they still
+  // write LDS) finish before any wave of the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   const float lt = other_half_sum(l);  // both halves of a row share row_ok
   if (!row_ok) return;
