@@ -74,6 +74,17 @@ constexpr int kVmcnt8 = waitcnt_vm(8);
 // every fragment address is a lane base plus an immediate.
 __device__ __forceinline__ int tile_off(int t, int ch) { return (t >> 1) * PAIR + (t & 1) * 512 + ch * 2; }
 
+// Token of the tile in slot m (0..31) of the S^T rows and of the P.V sums.
+// Any permutation is correct as long as K, V and the mask agree (the
+// products sum over tokens); this one spreads LDS reads over the banks: the
+// 8 K rows read together by lanes m..m+7 lie in 8 different 16-byte slots
+// of a 128-byte bank line, and the 4 V rows of a transpose read lie in 4
+// disjoint 32-byte spans (rows of a pair are 512 bytes apart, i.e. on the
+// same banks, so neighbouring slots take tokens from different pairs).
+__device__ __forceinline__ int tok_of(int m) {
+  return 16 * ((m >> 3) & 1) + 4 * (m & 3) + 2 * ((m >> 2) & 1) + (m >> 4);
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // (i % 4) of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.
 __device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
@@ -239,15 +250,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // Lane roles in the transpose reads of V (A operand of O^T): the lane is
   // k = lane % 16 of a 16-lane group; it supplies the address of token
   // row tok(k / 4) at channels 4 * (k % 4) of the group's 16-channel slice.
+  // For the chunk c of 16 slots, the lane addresses slot 16c + 4*half +
+  // kq/4 (first read) and 16c + 8 + 4*half + kq/4 (second read), i.e.
+  // tokens 4*(kq/4) + 2*half + c and 16 + the same: pairs 2*(kq/4) + half
+  // and 8 + that, row c.
   const int grp = lane >> 4, kq = lane & 15;
   const int vd0 = 16 * (grp & 1) + 4 * (kq & 3);  // channel within the 32-channel tile
-  const int vtok = 4 * half + (kq >> 2);          // token offset (+16c, +8)
+  const int vpair = 2 * (kq >> 2) + half;
 
   // Tiles are issued unconditionally: one past the last needed token has an
   // empty resource, so it reads nothing and fills a stage no one reads with
   // zeros. Every step then issues the same 4 instructions per wave and the
   // compiler's wait counts stay exact (a conditional issue would make it
   // wait for every load before each LDS read).
+  // Waves 0-3 (one per SIMD) win the SIMD's issue arbitration: after each
+  // barrier they take the matrix core first, and their softmax then runs on
+  // the vector unit while the SIMD's other wave multiplies, instead of both
+  // waves of a SIMD doing the same phase at the same time.
+  if (wave < WAVES / 2) __builtin_amdgcn_s_setprio(1);
+
   // The query fragments must be in registers before the first tile loads
   // leave: a wait for them inside the loop would also wait for every tile
   // load in flight.
@@ -270,15 +291,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // S^T (32 tokens x 32 rows).
     f32x16 s0 = {};
-    const uint8_t *krow = kl + tile_off(l32, 8 * half);
+    const uint8_t *krow = kl + tile_off(tok_of(l32), 8 * half);
 #pragma unroll
     for (int k = 0; k < 16; ++k) s0 = mfma(*reinterpret_cast<const uint4 *>(krow + 32 * k), qf[k], s0);
-    // Element e of the accumulator is token 8*(e/4) + 4*half + e%4.
+    // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4.
     float z[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int tok = t0 + 8 * (e >> 2) + 4 * half + (e & 3);
+      const int tok = t0 + tok_of(8 * (e >> 2) + 4 * half + (e & 3));
       const float v = s0[e] * sl2;
       z[e] = tok < limit ? v : -INFINITY;
       mx = fmaxf(mx, z[e]);
@@ -295,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       m = mn;
     }
     // Weights as the B operand of O^T: chunk c takes elements 8c .. 8c+7,
-    // i.e. tokens 16c + 4*half + (0..3) and 16c + 8 + 4*half + (0..3).
+    // i.e. slots 16c + 4*half + (0..3) and 16c + 8 + 4*half + (0..3).
     uint4 pw[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -312,14 +333,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // O^T (32 channels x 32 rows per dt) += V^T . P^T. The A operand comes
     // from the row-major V tile through two transpose reads whose token
     // order matches the weights'.
-    const uint8_t *vbase = vl + tile_off(vtok, vd0);
+    const uint8_t *vbase = vl + vpair * PAIR + 2 * vd0;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // tokens 16c + vtok and 16c + 8 + vtok: 8 and 4 token pairs further
-        const uint64_t va = tr_read(vbase + c * 8 * PAIR + dt * 64);
-        const uint64_t vb = tr_read(vbase + c * 8 * PAIR + 4 * PAIR + dt * 64);
+        // row c of pair vpair, and of pair vpair + 8
+        const uint64_t va = tr_read(vbase + c * 512 + dt * 64);
+        const uint64_t vb = tr_read(vbase + c * 512 + 8 * PAIR + dt * 64);
         const uint4 a = make_uint4((uint32_t)va, (uint32_t)(va >> 32), (uint32_t)vb,
                                    (uint32_t)(vb >> 32));
         o[dt] = mfma(a, pw[c], o[dt]);
