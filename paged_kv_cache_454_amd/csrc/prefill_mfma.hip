@@ -103,12 +103,21 @@ __device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
 // a barrier) before any wave reads the stage they fill; vector memory
 // operations complete in order, so the compiler's own waits for other loads
 // stay correct (they only become stricter).
+// M0 (the LDS address of the load) is saved and restored inside the
+// statement, and the one wait state between writing M0 and the load that
+// reads it is an explicit s_nop.
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_load16(u32x4v rsrc, uint32_t lds_addr, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory");
 }
 
 // Buffer resource over [base, base + bytes): raw buffer, no stride, the
