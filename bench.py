@@ -7,7 +7,7 @@ the needed size - run as 16 independent layers back to back.
 
 One step = for each of the 16 layers: the slot-mapped write of the step's
 new K/V (pa_reshape_and_cache), split-context decode (pa_decode_partitioned,
-512-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
+1024-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
 slot mappings come from the host allocator's layout before timing starts;
 every input is resident in HBM when the timed region begins.
 
@@ -41,6 +41,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_persistent_mixed_64seq_hbm_counters.md")
 TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
                    for f in ("decode_persistent.hip", "pa_device.h")]
+PREFILL_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "prefill_mfma_chunked_16x512.md")
+PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
+                           for f in ("prefill_mfma.hip", "pa_device.h")]
+# Partition size per workload: the long-context configuration fixes 512
+# tokens; for the others it is the fastest measured on MI355X (mixed
+# 16-layer step: 1.450 ms at 512, 1.376 ms at 1024, 1.373 ms at 2048).
+DEFAULT_PARTITION = {"mixed": 1024, "long": 512, "uniform": 256}
 WORKLOAD_NAMES = {
     "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
     "long": "long-context split decode, 4 seqs {8192, 16384, 32768, 32768}, bs 32",
@@ -54,7 +61,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-context partition in tokens (default: 1024 for the mixed "
+                         "workload, 512 for the long one as its configuration states, 256 "
+                         "for the uniform one)")
     ap.add_argument("--workload", default="mixed", choices=["mixed", "long", "uniform"],
                     help="decode workload (default: the mixed-length 16-layer batch)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -101,14 +111,15 @@ def cpu_baseline(seed, budget_s):
                       f"{done_seqs / dt / 16:.3f}"}
 
 
-def counted_traffic(workload, partition_size, seed):
-    """The counter record's HBM bytes per decode launch, or None when the record
-    was taken on another workload or the kernel's source has changed since."""
+def counted_traffic(workload, partition_size, seed, record=TRAFFIC_RECORD,
+                    sources=TRAFFIC_SOURCES):
+    """A counter record's HBM bytes per launch, or None when the record was
+    taken on another workload or the kernel's source has changed since."""
     try:
-        text = open(TRAFFIC_RECORD).read()
+        text = open(record).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
         h = hashlib.sha256()
-        for f in TRAFFIC_SOURCES:
+        for f in sources:
             with open(f, "rb") as fh:
                 h.update(fh.read())
     except (OSError, AttributeError, ValueError):
@@ -174,7 +185,9 @@ def prefill_leg(seed, reps, dev):
         "prefill_us": round(p_ms * 1e3, 2), "tflops": round(tf, 1),
         "roofline": {"bound": "mfma", "kernel": "pa_prefill_chunk", "achieved": round(tf, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": counted_traffic("prefill", None, seed, PREFILL_TRAFFIC_RECORD,
+                                                PREFILL_TRAFFIC_SOURCES)},
         "kv_context_bytes": kv_bytes,
         "write_us": round(w_ms * 1e3, 2),
         "write_gbs": round(w_bytes / (w_ms * 1e-3) / 1e9, 1),
@@ -200,7 +213,7 @@ def main():
     layers_n = inputs.PRESETS[W].get("layers", 1)
     layers, meta = inputs.device_decode_layers(W, args.seed, layers_n, dev)
     lens = meta["lens"]
-    P = args.partition_size
+    P = args.partition_size or DEFAULT_PARTITION[W]
     S = len(lens)
     hq, d = layers[0]["query"].shape[1], layers[0]["query"].shape[2]
     max_parts = max(1, math.ceil(int(lens.max()) / P))
