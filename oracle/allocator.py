@@ -21,6 +21,27 @@ Readings where the pages leave a step open (also listed in the design notes):
   empty queue is an out-of-blocks error.
 * The initial order of the free queue is an input (identity by default), so a
   seeded scatter of physical blocks is passed in, never drawn here.
+
+Copy-on-write sharing ("vLLM Architecture, Memory and Benchmarks Deep Dive",
+section 2, the "Copy-on-Write (CoW) Branching" item: rollouts forked from one
+prompt share its physical blocks, and a block is duplicated only when the
+rollouts diverge). Readings where the page leaves the mechanics open:
+* Every physical block carries a count of the block tables that hold it. A
+  fork gives the child a copy of the parent's table and length and raises the
+  count of each of those blocks; nothing is copied at fork time.
+* Sequences only grow, so a shared block that is full is never written again
+  and stays shared. The one block a sequence writes into is its last one while
+  it has free slots: an append into a last block that is shared and not full
+  first takes a fresh block (from the front of the free queue, before any
+  blocks for the growth), records the copy (old block -> fresh block), drops
+  one count from the old block and puts the fresh block in its place. The last
+  holder of a block (count 1) writes in place.
+* Releasing a sequence drops one count from each of its blocks; blocks whose
+  count reaches zero go to the back of the free queue, in the sequence's
+  logical order.
+* The recorded copies are taken by the caller once per step and applied to the
+  cache pools before that step's writes; the copy itself is the bitwise block
+  copy in ``attention.copy_blocks``.
 """
 
 from collections import deque
@@ -44,9 +65,27 @@ class BlockAllocatorModel:
         self.free_blocks = deque(order)
         self.tables = {}   # seq_id -> list of physical block ids, logical order
         self.lengths = {}  # seq_id -> tokens held
+        self.refs = {}     # physical block -> number of tables holding it
+        self.copies = []   # (source block, destination block) not yet taken
 
     def num_free(self):
         return len(self.free_blocks)
+
+    def fork(self, parent_id, child_id):
+        """Start ``child_id`` as a sharer of every block of ``parent_id``."""
+        if parent_id not in self.tables:
+            raise KeyError(parent_id)
+        if child_id in self.tables:
+            raise ValueError(f"sequence {child_id} already exists")
+        self.tables[child_id] = list(self.tables[parent_id])
+        self.lengths[child_id] = self.lengths[parent_id]
+        for b in self.tables[child_id]:
+            self.refs[b] += 1
+
+    def take_copies(self):
+        """The block copies recorded since the last call, in order."""
+        out, self.copies = self.copies, []
+        return out
 
     def append(self, seq_id, num_tokens):
         """Grow ``seq_id`` by ``num_tokens`` tokens and return their slots.
@@ -59,12 +98,23 @@ class BlockAllocatorModel:
         table = self.tables.get(seq_id, [])
         have = len(table)
         want = -(-(held + num_tokens) // self.block_size)
-        if want - have > len(self.free_blocks):
+        # Writing into a shared last block that still has room needs a copy.
+        cow = num_tokens > 0 and held % self.block_size != 0 and self.refs[table[-1]] > 1
+        if want - have + cow > len(self.free_blocks):
             raise OutOfBlocks(
-                f"sequence {seq_id}: needs {want - have} blocks, {len(self.free_blocks)} free")
+                f"sequence {seq_id}: needs {want - have + cow} blocks, "
+                f"{len(self.free_blocks)} free")
         table = list(table)
+        if cow:
+            fresh = self.free_blocks.popleft()
+            self.copies.append((table[-1], fresh))
+            self.refs[table[-1]] -= 1
+            self.refs[fresh] = 1
+            table[-1] = fresh
         for _ in range(want - have):
-            table.append(self.free_blocks.popleft())
+            b = self.free_blocks.popleft()
+            self.refs[b] = 1
+            table.append(b)
         self.tables[seq_id] = table
         self.lengths[seq_id] = held + num_tokens
         slots = []
@@ -73,10 +123,15 @@ class BlockAllocatorModel:
         return slots
 
     def free(self, seq_id):
-        """Return every block of ``seq_id`` to the back of the free queue."""
+        """Release ``seq_id``: its blocks that no other table holds go to the
+        back of the free queue (in logical order)."""
         if seq_id not in self.tables:
             raise KeyError(seq_id)
-        self.free_blocks.extend(self.tables.pop(seq_id))
+        for b in self.tables.pop(seq_id):
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                del self.refs[b]
+                self.free_blocks.append(b)
         del self.lengths[seq_id]
 
     def block_table(self, seq_ids, max_blocks, pad=-1):

@@ -52,6 +52,25 @@ def cache_write(key_cache, value_cache, key, value, slot_mapping, block_size):
     return kc, vc
 
 
+def copy_blocks(key_cache, value_cache, block_pairs):
+    """Copy-on-write duplication ("vLLM Architecture, Memory and Benchmarks
+    Deep Dive", section 2, "Copy-on-Write (CoW) Branching": a shared block is
+    cloned when the sequences holding it diverge) applied to copies of both
+    pools: for each (src, dst) pair, every KV head and token row of block src
+    is written to block dst. Pairs whose ids fall outside the pool are
+    skipped. The destinations are distinct and never a source of another
+    pair, so the pairs are independent. A bit copy."""
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    nb = kc.shape[0]
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        if not (0 <= src < nb and 0 <= dst < nb):
+            continue
+        kc[dst] = key_cache[src]
+        vc[dst] = value_cache[src]
+    return kc, vc
+
+
 def gather_context(cache, block_table_row, context_len, block_size):
     """Logical [context_len][num_kv_heads][head_dim] view of one sequence's
     cache, rebuilt position by position through its block table."""

@@ -229,6 +229,95 @@ def pin_allocator_invariants(alloc):
     assert b.num_free() == 0 and 2 not in b.tables
 
 
+def _cow_state_ok(a):
+    held = {}
+    for table in a.tables.values():
+        for b in table:
+            held[b] = held.get(b, 0) + 1
+    assert held == a.refs                                 # counts = tables holding each block
+    assert not set(held) & set(a.free_blocks)
+    assert len(held) + a.num_free() == a.num_blocks
+
+
+def pin_cow_contents(alloc):
+    """Copy-on-write judged by what each sequence reads back: a token marker
+    is written at every appended slot of a simulated pool, recorded copies
+    duplicate whole blocks before the writes, and every live sequence must
+    then read, through its table, exactly its own history (its ancestors'
+    tokens up to the fork, then its own), whatever its siblings wrote."""
+    rng = random.Random(11)
+    for bs, nb in ((4, 48), (1, 30), (5, 40)):
+        a = alloc.BlockAllocatorModel(nb, bs)
+        pool = [[None] * bs for _ in range(nb)]
+        history = {}
+        mark = 0
+        for _ in range(600):
+            op = rng.random()
+            live = sorted(history)
+            if op < 0.5 or not live:
+                sid = rng.choice(live) if live and rng.random() < 0.8 else rng.randrange(1000)
+                n = rng.randint(0, 2 * bs + 1)
+                try:
+                    slots = a.append(sid, n)
+                except alloc.OutOfBlocks:
+                    assert a.take_copies() == []
+                    continue
+                for src, dst in a.take_copies():
+                    pool[dst] = list(pool[src])
+                for slot in slots:
+                    mark += 1
+                    pool[slot // bs][slot % bs] = mark
+                    history.setdefault(sid, []).append(mark)
+                history.setdefault(sid, [])
+            elif op < 0.75:
+                parent = rng.choice(live)
+                child = 1000 + rng.randrange(1000)
+                if child in history:
+                    continue
+                a.fork(parent, child)
+                history[child] = list(history[parent])
+            else:
+                sid = rng.choice(live)
+                a.free(sid)
+                del history[sid]
+            for sid, hist in history.items():
+                t = a.tables[sid]
+                assert a.lengths[sid] == len(hist)
+                assert [pool[t[p // bs]][p % bs] for p in range(len(hist))] == hist, sid
+            _cow_state_ok(a)
+
+
+def pin_cow_counts(alloc):
+    """A prompt whose last block is partly filled, forked k times: nothing is
+    copied at fork time; when each of the k+1 holders appends a token, the
+    first k copy the shared block and the last writes in place. With a full
+    last block no append copies anything."""
+    for k in (1, 3, 7):
+        a = alloc.BlockAllocatorModel(64, 4)
+        a.append(0, 10)                                   # blocks 0, 1, 2 (2 slots free)
+        for c in range(1, k + 1):
+            a.fork(0, c)
+        assert a.take_copies() == [] and a.num_free() == 61
+        for c in range(k + 1):
+            a.append(c, 1)
+        cp = a.take_copies()
+        assert len(cp) == k and all(src == 2 for src, _ in cp)
+        assert [dst for _, dst in cp] == list(range(3, 3 + k))  # from the front, in order
+        assert a.num_free() == 61 - k
+        b = alloc.BlockAllocatorModel(64, 4)
+        b.append(0, 8)                                    # two full blocks
+        for c in range(1, k + 1):
+            b.fork(0, c)
+        for c in range(k + 1):
+            b.append(c, 3)
+        assert b.take_copies() == [] and b.num_free() == 62 - (k + 1)
+        # the shared blocks survive until their last holder is released
+        for c in range(k + 1):
+            before = b.num_free()
+            b.free(c)
+            assert b.num_free() - before == 1 + (2 if c == k else 0)
+
+
 # -------------------------------------------------------------- attention
 
 def pin_cache_write(attn):
@@ -411,8 +500,27 @@ def pin_prefill(attn):
             assert np.abs(out[qsl[s] + j] - want).max() < 1e-12
 
 
+def pin_copy_blocks(attn):
+    """Block copies against element-wise loops over a pool of distinct
+    values: every destination block equals its source in all heads and rows,
+    other blocks are untouched, and out-of-range pairs change nothing."""
+    rng = np.random.default_rng(5)
+    kc = rng.standard_normal((9, 2, 3, 4))
+    vc = rng.standard_normal((9, 2, 3, 4))
+    pairs = [(1, 4), (7, 0), (2, 8), (-1, 3), (5, 9)]
+    k2, v2 = attn.copy_blocks(kc, vc, pairs)
+    for b in range(9):
+        src = {4: 1, 0: 7, 8: 2}.get(b, b)
+        for h in range(2):
+            for r in range(3):
+                for c in range(4):
+                    assert k2[b, h, r, c] == kc[src, h, r, c]
+                    assert v2[b, h, r, c] == vc[src, h, r, c]
+
+
 ATTENTION_PINS = [pin_cache_write, pin_decode_bruteforce, pin_decode_vs_library,
                   pin_decode_special_cases, pin_permutation_invariance, pin_partitions,
-                  pin_prefill]
+                  pin_prefill, pin_copy_blocks]
 ACCOUNTING_PINS = [pin_kv_size, pin_worked_example_accounting]
-ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants]
+ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants, pin_cow_contents,
+                  pin_cow_counts]

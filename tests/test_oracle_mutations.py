@@ -39,11 +39,26 @@ MUTATIONS = [
     ("accounting", "return 2 * num_layers * num_kv_heads", "return num_layers * num_kv_heads"),
     ("accounting", "return -(-num_tokens // block_size)", "return num_tokens // block_size"),
     ("accounting", "reserved = len(token_counts) * max_len", "reserved = sum(token_counts)"),
-    ("allocator", "table.append(self.free_blocks.popleft())",
-     "table.append(self.free_blocks.pop())"),
-    ("allocator", "self.free_blocks.extend(self.tables.pop(seq_id))",
-     "self.free_blocks.extendleft(self.tables.pop(seq_id))"),
-    ("allocator", "if want - have > len(self.free_blocks):", "if want - have > len(self.free_blocks) + 1:"),
+    ("allocator", "            b = self.free_blocks.popleft()",
+     "            b = self.free_blocks.pop()"),
+    ("allocator", "            fresh = self.free_blocks.popleft()",
+     "            fresh = self.free_blocks.pop()"),
+    ("allocator", "                self.free_blocks.append(b)",
+     "                self.free_blocks.appendleft(b)"),
+    ("allocator", "self.refs[table[-1]] > 1", "self.refs[table[-1]] > 0"),
+    ("allocator", "self.refs[table[-1]] > 1", "self.refs[table[-1]] > 2"),
+    ("allocator", "self.copies.append((table[-1], fresh))", "self.copies.append((fresh, table[-1]))"),
+    ("allocator", "            self.refs[table[-1]] -= 1\n", "\n"),
+    ("allocator", "            if self.refs[b] == 0:", "            if self.refs[b] <= 1:"),
+    ("allocator", "            self.refs[b] += 1", "            self.refs[b] += 0"),
+    ("allocator", "cow = num_tokens > 0 and held % self.block_size != 0",
+     "cow = num_tokens > 0"),
+    ("attention", "        kc[dst] = key_cache[src]", "        kc[src] = key_cache[dst]"),
+    ("attention", "        vc[dst] = value_cache[src]", "        vc[dst] = key_cache[src]"),
+    ("allocator", "if want - have + cow > len(self.free_blocks):",
+     "if want - have + cow > len(self.free_blocks) + 1:"),
+    ("allocator", "if want - have + cow > len(self.free_blocks):",
+     "if want - have > len(self.free_blocks):"),
     ("allocator", "want = -(-(held + num_tokens) // self.block_size)",
      "want = (held + num_tokens) // self.block_size + 1"),
 ]
