@@ -93,6 +93,25 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
                                hipStream_t stream);
 
 /*
+ * pa_copy_blocks - apply copy-on-write clones ([P2] s.2 "Copy-on-Write (CoW)
+ * Branching": a block shared by forked sequences is duplicated when they
+ * diverge; pa_alloc_take_copies lists the pairs). For each pair, all
+ * num_kv_heads x block_size rows of block src are copied to block dst, in
+ * both pools.
+ *  key_cache,
+ *  value_cache  [device] kv_dtype pools (layout above), updated in place
+ *  block_pairs  [device] int32 [num_pairs][2] = (src, dst)
+ * A pair with an id outside [0, num_blocks), or with src == dst, is skipped.
+ * Destinations must be distinct and never the source of another pair (the
+ * allocator's pairs are); otherwise the result is unspecified. A bit copy.
+ * num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype kv_dtype,
+                         hipStream_t stream);
+
+/*
  * pa_decode - single-pass paged decode attention: one query token per
  * sequence attends over its whole paged context ([P3] PagedAttention section:
  * the scattered blocks "appear contiguous to the attention mechanism").
@@ -226,9 +245,32 @@ void pa_alloc_destroy(pa_alloc *a);
  * All or nothing: on PA_ENOMEM nothing changes. */
 pa_status pa_alloc_append(pa_alloc *a, int64_t seq_id, int32_t num_tokens, int64_t *slots_out);
 
-/* Return all blocks of seq_id to the back of the free queue (in the
- * sequence's logical order) and forget it. PA_ENOTFOUND if unknown. */
+/* Release seq_id and forget it: each of its blocks loses one holder, and
+ * the blocks no other sequence holds go to the back of the free queue (in the
+ * sequence's logical order). PA_ENOTFOUND if unknown. */
 pa_status pa_alloc_free(pa_alloc *a, int64_t seq_id);
+
+/* Copy-on-write branching ([P2] s.2 "Copy-on-Write (CoW) Branching": forked
+ * rollouts share the prompt's physical blocks, cloned only when they
+ * diverge). Start child_id as a sharer of every block of parent_id (same
+ * table, same length); nothing is copied now. PA_ENOTFOUND if parent_id is
+ * unknown, PA_EINVAL if child_id exists.
+ * Appends then copy on write: an append to a sequence whose last block is
+ * shared and has free slots first takes a fresh block from the front of the
+ * free queue and queues the copy (old block -> fresh block); the last holder
+ * of a block writes in place. The queued copies must be applied to both pools
+ * (pa_copy_blocks) before the step's new K/V are written. */
+pa_status pa_alloc_fork(pa_alloc *a, int64_t parent_id, int64_t child_id);
+
+/* Take the queued copies: pairs_out [host] int32 [max_pairs][2] receives
+ * (source, destination) block ids in the order they were queued and the
+ * queue is emptied. Returns the number of queued pairs; if that exceeds
+ * max_pairs nothing is taken (call again with room for that many). -1 for a
+ * NULL allocator or bad arguments. */
+int32_t pa_alloc_take_copies(pa_alloc *a, int32_t *pairs_out, int32_t max_pairs);
+
+/* Number of sequences holding block (0 = free), or -1 if out of range. */
+int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block);
 
 /* Free blocks in the pool; -1 if a is NULL. */
 int32_t pa_alloc_num_free(const pa_alloc *a);

@@ -5,8 +5,8 @@ The compute path is libpa.so (hand-written HIP kernels behind a C ABI,
 it (``binding``). ``inputs`` holds the seeded synthetic workloads.
 """
 
-from .binding import (BlockAllocator, PAError, pa_decode, pa_decode_partitioned,  # noqa: F401
-                      pa_partition_workspace_bytes, pa_prefill_chunk, pa_reduce,
-                      pa_reshape_and_cache)
+from .binding import (BlockAllocator, PAError, pa_copy_blocks, pa_decode,  # noqa: F401
+                      pa_decode_partitioned, pa_partition_workspace_bytes, pa_prefill_chunk,
+                      pa_reduce, pa_reshape_and_cache)
 
 __version__ = "0.1.0"

@@ -26,6 +26,7 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_st, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st, _p]),
+    "pa_copy_blocks": (_st, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st, _p]),
     "pa_decode": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _st, _st, _p]),
     "pa_partition_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
@@ -41,6 +42,9 @@ SIGNATURES = {
     "pa_alloc_num_free": (_i32, [_p]),
     "pa_alloc_seq_len": (_i32, [_p, _i64]),
     "pa_alloc_block_table": (_st, [_p, _p, _i32, _i32, _p, _p]),
+    "pa_alloc_fork": (_st, [_p, _i64, _i64]),
+    "pa_alloc_take_copies": (_i32, [_p, _p, _i32]),
+    "pa_alloc_block_refs": (_i32, [_p, _i32]),
 }
 
 _LIB = None

@@ -71,6 +71,18 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
                                      _dtype(key_cache, "pools"), _stream(stream)))
 
 
+def pa_copy_blocks(key_cache, value_cache, block_pairs, stream=None):
+    """Copy whole blocks inside both pools: block_pairs is int32 [n][2] of
+    (source, destination) ids (the allocator's copy-on-write pairs)."""
+    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [num_pairs][2]")
+    n = block_pairs.shape[0]
+    check(lib().pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                               _dev(block_pairs, "block_pairs", torch.int32), n, hkv, d, bs,
+                               num_blocks, _dtype(key_cache, "pools"), _stream(stream)))
+
+
 def _attn_common(query, key_cache, value_cache, block_tables, context_lens, rows_name):
     num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
     if query.dim() != 3 or query.shape[2] != d:
@@ -210,6 +222,26 @@ class BlockAllocator:
 
     def seq_len(self, seq_id):
         return int(lib().pa_alloc_seq_len(self._h, int(seq_id)))
+
+    def fork(self, parent_id, child_id):
+        """Start child_id as a sharer of all of parent_id's blocks (copy on write)."""
+        check(lib().pa_alloc_fork(self._h, int(parent_id), int(child_id)))
+
+    def take_copies(self):
+        """Queued copy-on-write pairs as int32 [n][2] (source, destination);
+        the queue is emptied."""
+        n = int(lib().pa_alloc_take_copies(self._h, None, 0))
+        if n < 0:
+            raise PAError(-1, "pa_alloc_take_copies failed")
+        pairs = np.empty((n, 2), dtype=np.int32)
+        if n:
+            got = int(lib().pa_alloc_take_copies(self._h, pairs.ctypes.data, n))
+            if got != n:
+                raise PAError(-1, "pa_alloc_take_copies: queue changed")
+        return pairs
+
+    def block_refs(self, block):
+        return int(lib().pa_alloc_block_refs(self._h, int(block)))
 
     def block_table(self, seq_ids, max_blocks):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)

@@ -11,6 +11,16 @@
 // The queue is a ring buffer of block ids (capacity = pool size), so taking
 // and returning blocks is O(1) per block with no allocation on the hot path;
 // sequences live in a hash map keyed by their 64-bit id.
+//
+// Copy-on-write sharing ("vLLM Architecture, Memory and Benchmarks Deep
+// Dive", section 2, "Copy-on-Write (CoW) Branching": forked rollouts share
+// the prompt's blocks, which are cloned only when the rollouts diverge).
+// Every block carries the number of tables that hold it. A fork copies the
+// parent's table and raises those counts; an append into a last block that is
+// shared and not yet full first takes a fresh block from the front of the
+// queue, records the pending copy (old -> fresh) and swaps it in; a release
+// returns only the blocks whose count drops to zero. Full shared blocks are
+// never written again (sequences only grow), so they stay shared.
 #include <cstdint>
 #include <new>
 #include <unordered_map>
@@ -24,6 +34,8 @@ struct pa_alloc {
   std::vector<int32_t> ring;  // free queue storage, capacity num_blocks
   int64_t head = 0;           // index of the front element
   int64_t count = 0;          // elements in the queue
+  std::vector<int32_t> refs;  // tables holding each block (0 = free)
+  std::vector<int32_t> copies;  // pending (source, destination) pairs, flattened
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t len = 0;
@@ -54,6 +66,7 @@ extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
   if (!a) return pa::fail(PA_ENOMEM, "pa_alloc_create: host allocation failed");
   try {
     a->ring.resize(num_blocks);
+    a->refs.assign(num_blocks, 0);
   } catch (...) {
     delete a;
     return pa::fail(PA_ENOMEM, "pa_alloc_create: host allocation failed");
@@ -93,18 +106,34 @@ extern "C" pa_status pa_alloc_append(pa_alloc *a, int64_t seq_id, int32_t num_to
   const int64_t held = it == a->seqs.end() ? 0 : it->second.len;
   const int64_t have = it == a->seqs.end() ? 0 : (int64_t)it->second.blocks.size();
   const int64_t want = (held + num_tokens + a->block_size - 1) / a->block_size;
-  if (want - have > a->count)
+  // Writing into a shared last block that still has room needs a copy.
+  const bool cow = num_tokens > 0 && held % a->block_size != 0 &&
+                   a->refs[it->second.blocks.back()] > 1;
+  if (want - have + cow > a->count)
     return pa::fail(PA_ENOMEM, "pa_alloc_append: sequence %lld needs %lld blocks, %lld free",
-                    (long long)seq_id, (long long)(want - have), (long long)a->count);
+                    (long long)seq_id, (long long)(want - have + cow), (long long)a->count);
   pa_alloc::Seq *s;
   try {
     s = &a->seqs[seq_id];
     s->blocks.reserve(want);
+    if (cow) a->copies.reserve(a->copies.size() + 2);
   } catch (...) {
     if (it == a->seqs.end()) a->seqs.erase(seq_id);
     return pa::fail(PA_ENOMEM, "pa_alloc_append: host allocation failed");
   }
-  for (int64_t i = have; i < want; ++i) s->blocks.push_back(a->pop_front());
+  if (cow) {
+    const int32_t old = s->blocks.back(), fresh = a->pop_front();
+    a->copies.push_back(old);
+    a->copies.push_back(fresh);
+    --a->refs[old];
+    a->refs[fresh] = 1;
+    s->blocks.back() = fresh;
+  }
+  for (int64_t i = have; i < want; ++i) {
+    const int32_t b = a->pop_front();
+    a->refs[b] = 1;
+    s->blocks.push_back(b);
+  }
   if (slots_out) {
     for (int32_t i = 0; i < num_tokens; ++i) {
       const int64_t pos = held + i;
@@ -121,9 +150,43 @@ extern "C" pa_status pa_alloc_free(pa_alloc *a, int64_t seq_id) {
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end())
     return pa::fail(PA_ENOTFOUND, "pa_alloc_free: unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.blocks) a->push_back(b);
+  for (int32_t b : it->second.blocks)
+    if (--a->refs[b] == 0) a->push_back(b);
   a->seqs.erase(it);
   return PA_OK;
+}
+
+extern "C" pa_status pa_alloc_fork(pa_alloc *a, int64_t parent_id, int64_t child_id) {
+  pa::clear_error();
+  if (!a) return pa::fail(PA_EINVAL, "pa_alloc_fork: allocator is NULL");
+  auto it = a->seqs.find(parent_id);
+  if (it == a->seqs.end())
+    return pa::fail(PA_ENOTFOUND, "pa_alloc_fork: unknown sequence %lld", (long long)parent_id);
+  if (a->seqs.count(child_id))
+    return pa::fail(PA_EINVAL, "pa_alloc_fork: sequence %lld already exists",
+                    (long long)child_id);
+  try {
+    pa_alloc::Seq child = it->second;  // copy before the map may rehash
+    a->seqs.emplace(child_id, std::move(child));
+  } catch (...) {
+    return pa::fail(PA_ENOMEM, "pa_alloc_fork: host allocation failed");
+  }
+  for (int32_t b : a->seqs[child_id].blocks) ++a->refs[b];
+  return PA_OK;
+}
+
+extern "C" int32_t pa_alloc_take_copies(pa_alloc *a, int32_t *pairs_out, int32_t max_pairs) {
+  if (!a || max_pairs < 0 || (max_pairs > 0 && !pairs_out)) return -1;
+  const int64_t n = (int64_t)a->copies.size() / 2;
+  if (n > max_pairs) return (int32_t)n;  // nothing taken; ask again with room for n
+  for (int64_t i = 0; i < 2 * n; ++i) pairs_out[i] = a->copies[i];
+  a->copies.clear();
+  return (int32_t)n;
+}
+
+extern "C" int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->refs[block];
 }
 
 extern "C" int32_t pa_alloc_num_free(const pa_alloc *a) { return a ? (int32_t)a->count : -1; }

@@ -1,0 +1,95 @@
+// Whole-block copies inside the two pools, for copy-on-write sharing
+// ("vLLM Architecture, Memory and Benchmarks Deep Dive", section 2,
+// "Copy-on-Write (CoW) Branching": a shared block is cloned when the
+// sequences holding it diverge).
+//
+// A block is contiguous in each pool ([num_kv_heads][block_size][head_dim]),
+// so a copy is a straight memcpy of block_bytes. Grid: x = 16 KiB slices of
+// a block, y = pairs. Each thread issues all of its K and V loads of a slice
+// before the stores, so a workgroup keeps 32 KiB in flight. The pair is read
+// once per workgroup (the same address in every lane); pairs with an id
+// outside the pool, or with source equal to destination, do nothing.
+#include "launch.h"
+#include "pa_device.h"
+
+namespace pa {
+
+template <int UNIT>
+struct CopyUnit;
+template <>
+struct CopyUnit<16> {
+  using T = vec16;
+};
+template <>
+struct CopyUnit<4> {
+  using T = uint32_t;
+};
+template <>
+struct CopyUnit<2> {
+  using T = uint16_t;
+};
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+template <int UNIT>
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint8_t *__restrict__ key_cache, uint8_t *__restrict__ value_cache,
+    const int32_t *__restrict__ pairs, int32_t num_pairs, int32_t num_blocks,
+    int64_t block_bytes) {
+  using T = typename CopyUnit<UNIT>::T;
+  const int64_t units = block_bytes / UNIT;
+  for (int32_t pr = blockIdx.y; pr < num_pairs; pr += gridDim.y) {
+    const int32_t src = pairs[2 * pr], dst = pairs[2 * pr + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) continue;
+    const T *ks = reinterpret_cast<const T *>(key_cache + (int64_t)src * block_bytes);
+    const T *vs = reinterpret_cast<const T *>(value_cache + (int64_t)src * block_bytes);
+    T *kd = reinterpret_cast<T *>(key_cache + (int64_t)dst * block_bytes);
+    T *vd = reinterpret_cast<T *>(value_cache + (int64_t)dst * block_bytes);
+    for (int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll; base < units;
+         base += (int64_t)gridDim.x * kCopyThreads * kCopyUnroll) {
+      T k[kCopyUnroll], v[kCopyUnroll];
+#pragma unroll
+      for (int i = 0; i < kCopyUnroll; ++i) {
+        const int64_t u = base + i * kCopyThreads + threadIdx.x;
+        if (u < units) {
+          k[i] = ks[u];
+          v[i] = vs[u];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kCopyUnroll; ++i) {
+        const int64_t u = base + i * kCopyThreads + threadIdx.x;
+        if (u < units) {
+          kd[u] = k[i];
+          vd[u] = v[i];
+        }
+      }
+    }
+  }
+}
+
+pa_status launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs,
+                             int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                             hipStream_t stream) {
+  const int unit = (block_bytes % 16 == 0) ? 16 : (block_bytes % 4 == 0) ? 4 : 2;
+  const int64_t units = block_bytes / unit;
+  int64_t gx = (units + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
+  if (gx > 1024) gx = 1024;  // the slice loop covers the rest
+  const unsigned gy = (unsigned)(num_pairs < 65535 ? num_pairs : 65535);
+  const dim3 grid((unsigned)gx, gy);
+  auto kc = (uint8_t *)key_cache;
+  auto vc = (uint8_t *)value_cache;
+  if (unit == 16)
+    copy_blocks_kernel<16><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
+                                                              num_blocks, block_bytes);
+  else if (unit == 4)
+    copy_blocks_kernel<4><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
+                                                             num_blocks, block_bytes);
+  else
+    copy_blocks_kernel<2><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
+                                                             num_blocks, block_bytes);
+  return check_launch("pa_copy_blocks");
+}
+
+}  // namespace pa

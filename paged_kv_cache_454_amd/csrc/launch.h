@@ -7,6 +7,10 @@
 
 namespace pa {
 
+pa_status launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs,
+                             int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                             hipStream_t stream);
+
 pa_status launch_cache_write(const void *key, const void *value, void *key_cache,
                              void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

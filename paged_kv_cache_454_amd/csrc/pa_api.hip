@@ -61,6 +61,26 @@ extern "C" pa_status pa_reshape_and_cache(const void *key, const void *value, vo
                                 dtype_bytes(kv_dtype), stream);
 }
 
+extern "C" pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_pairs,
+                                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, pa_dtype kv_dtype,
+                                    hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_copy_blocks";
+  if (num_pairs < 0) return pa::fail(PA_EINVAL, "%s: num_pairs=%d < 0", fn, num_pairs);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa::fail(PA_EINVAL, "%s: num_kv_heads=%d head_dim=%d block_size=%d num_blocks=%d", fn,
+                    num_kv_heads, head_dim, block_size, num_blocks);
+  if (!dtype_ok(kv_dtype)) return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_pairs)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  const int64_t block_bytes =
+      (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
+  return pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs, block_bytes,
+                                num_blocks, stream);
+}
+
 extern "C" pa_status pa_decode(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -85,3 +85,76 @@ def test_errors():
     a.free(7)
     assert a.num_free() == 2
     assert list(a.append(8, 5)) == [0, 1, 2, 3, 4]             # FIFO reuse: 0 then 1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cow_matches_oracle_model(seed):
+    """Appends, forks and releases in random order: the native allocator and
+    the oracle's model give the same slots, tables, free counts, holder
+    counts and copy-on-write pairs at every step."""
+    rng = random.Random(100 + seed)
+    nb, bs = rng.choice([(24, 4), (64, 16), (40, 1), (30, 5)])
+    order = list(range(nb))
+    rng.shuffle(order)
+    a = BlockAllocator(nb, bs, initial_order=order)
+    m = model.BlockAllocatorModel(nb, bs, initial_order=order)
+    live = set()
+    for _ in range(400):
+        op = rng.random()
+        if op < 0.5 or not live:
+            sid = rng.choice(sorted(live)) if live and rng.random() < 0.8 else rng.randrange(50)
+            n = rng.randint(0, 2 * bs + 1)
+            try:
+                want = m.append(sid, n)
+            except model.OutOfBlocks:
+                with pytest.raises(PAError) as e:
+                    a.append(sid, n)
+                assert e.value.status == PA_ENOMEM
+                assert len(a.take_copies()) == 0 and m.take_copies() == []
+                continue
+            assert list(a.append(sid, n)) == want
+            live.add(sid)
+        elif op < 0.75:
+            parent = rng.choice(sorted(live))
+            child = rng.randrange(50, 100)
+            if child in live:
+                with pytest.raises(PAError) as e:
+                    a.fork(parent, child)
+                assert e.value.status == PA_EINVAL
+                continue
+            m.fork(parent, child)
+            a.fork(parent, child)
+            live.add(child)
+        else:
+            sid = rng.choice(sorted(live))
+            m.free(sid)
+            a.free(sid)
+            live.discard(sid)
+        assert [tuple(p) for p in a.take_copies().tolist()] == m.take_copies()
+        assert a.num_free() == m.num_free()
+        assert [a.block_refs(b) for b in range(nb)] == [m.refs.get(b, 0) for b in range(nb)]
+        if live:
+            ids = sorted(live)
+            maxb = max(len(m.tables[s]) for s in ids) + 1
+            t_m, l_m = m.block_table(ids, maxb)
+            t_a, l_a = a.block_table(ids, maxb)
+            assert np.array_equal(t_a, np.array(t_m, dtype=np.int32))
+            assert list(l_a) == l_m
+
+
+def test_fork_errors_and_copy_queue():
+    a = BlockAllocator(8, 4)
+    with pytest.raises(PAError) as e:
+        a.fork(1, 2)                                            # unknown parent
+    assert e.value.status == PA_ENOTFOUND
+    a.append(1, 6)                                              # blocks 0, 1 (half full)
+    a.fork(1, 2)
+    assert a.block_refs(0) == 2 and a.block_refs(1) == 2 and a.num_free() == 6
+    assert list(a.append(2, 1)) == [2 * 4 + 2]                  # copy of block 1 into block 2
+    assert list(a.append(1, 1)) == [1 * 4 + 2]                  # the last holder writes in place
+    assert a.take_copies().tolist() == [[1, 2]]
+    assert a.take_copies().shape == (0, 2)                      # emptied
+    a.free(1)
+    assert a.num_free() == 6 and a.block_refs(0) == 1           # block 0 still held by 2
+    a.free(2)
+    assert a.num_free() == 8
