@@ -74,7 +74,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
-                    help="timed repetitions of the chunked-prefill leg (0 skips it)")
+                    help="timed repetitions of the side legs, chunked prefill and "
+                         "copy-on-write block copies (0 skips them)")
     return ap.parse_args()
 
 
@@ -195,6 +196,52 @@ def prefill_leg(seed, reps, dev):
     }
 
 
+def cow_leg(seed, reps, dev):
+    """Copy-on-write fan-out: the 64 prompts of the mixed workload (layer
+    shape 4 KV heads x 16 tokens x 256, BF16) each forked into 16 rollouts
+    with the native allocator; the first decode step of every rollout
+    appends one token, which queues one block copy per rollout that shares a
+    partly filled last block. Times pa_copy_blocks on those pairs."""
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    from paged_kv_cache_454_amd import BlockAllocator, inputs
+    lens = [int(x) for x in inputs.preset_lengths("mixed", seed)]
+    bs, rollouts, hkv, d = 16, 16, 4, 256
+    nb = sum(-(-n // bs) for n in lens) + len(lens) * rollouts + 16
+    a = BlockAllocator(nb, bs)
+    for s, n in enumerate(lens):
+        a.append(s * rollouts, n)
+        for r in range(1, rollouts):
+            a.fork(s * rollouts, s * rollouts + r)
+    for s in range(len(lens)):
+        for r in range(rollouts):
+            a.append(s * rollouts + r, 1)
+    pairs = a.take_copies()
+    kc = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    pd = torch.from_numpy(pairs).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def copy():
+        pa.pa_copy_blocks(kc, vc, pd, stream=stream)
+
+    copy()
+    torch.cuda.synchronize()
+    ms = timed_launches(copy, reps, stream)
+    nbytes = 2 * 2 * len(pairs) * hkv * bs * d * 2   # K and V blocks, read and written
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "copy-on-write fan-out: 64 mixed-length prompts x 16 rollouts, first "
+                    "divergent step, blocks of 4 x 16 x 256 BF16",
+        "pairs": int(len(pairs)), "bytes": nbytes, "copy_us": round(ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_copy_blocks", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "reps": reps,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -301,6 +348,7 @@ def main():
         del layers, po, pm, ps, outs
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
+        result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)
     if args.cpu_seconds > 0 and W == "mixed":
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     if args.copy_calibration:
