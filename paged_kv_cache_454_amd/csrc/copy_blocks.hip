@@ -14,11 +14,13 @@
 
 namespace pa {
 
+typedef uint32_t copy_u32x4 __attribute__((ext_vector_type(4)));
+
 template <int UNIT>
 struct CopyUnit;
 template <>
 struct CopyUnit<16> {
-  using T = vec16;
+  using T = copy_u32x4;
 };
 template <>
 struct CopyUnit<4> {
