@@ -249,6 +249,74 @@ def cow_leg(seed, reps, dev):
     }
 
 
+def loop_leg(seed, steps, dev):
+    """Continuous-batching decode loop (``DecodeLoop``): 64 batch slots, 16
+    layers of the mixed workload's shape (24/4 heads, d 256, block 16,
+    1024-token partitions). Prompts are drawn log-uniform in [16, 8192] like
+    the mixed workload, generation lengths uniform in [16, 128]; a finished
+    request's slot is refilled at once (its prompt K/V written into all 16
+    layers). Times `steps` whole iterations (native allocator step, batch
+    upload, write + split decode + merge for 16 layers, releases and
+    admissions) after a warm-up, with eager launches and with the device part
+    replayed as a HIP graph."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_454_amd import inputs
+    from paged_kv_cache_454_amd.decode_loop import DecodeLoop
+    slots, layers, hq, hkv, d, bs, P = 64, 16, 24, 4, 256, 16, 1024
+    maxc = 8192 + 512
+    nb = slots * (maxc // bs) + 64
+    rng = np.random.default_rng(seed + 1)
+    prompt = torch.randn((layers, 8192, hkv, d), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for mode in ("eager", "graph"):
+        loop = DecodeLoop(slots=slots, num_blocks=nb, block_size=bs, layers=layers,
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, partition_size=P,
+                          max_context=maxc, device=dev, use_graph=(mode == "graph"))
+        loop.query.normal_()
+        loop.new_k.normal_()
+        loop.new_v.normal_()
+        nid = [0]
+        admitted = [0]
+
+        def admit(slot):
+            n = int(inputs.log_uniform_lengths(rng, 1, 16, 8192)[0])
+            loop.admit(slot, nid[0], n, int(rng.integers(16, 129)), prompt[:, :n], prompt[:, :n])
+            nid[0] += 1
+            admitted[0] += 1
+
+        for s in range(slots):
+            admit(s)
+
+        def iteration():
+            act = loop.step()
+            for s, _ in loop.finish_done():
+                admit(s)
+            return len(act)
+
+        for _ in range(5):
+            iteration()
+        torch.cuda.synchronize()
+        admitted[0] = 0
+        t0 = time.perf_counter()
+        tokens = sum(iteration() for _ in range(steps))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        res[mode] = {"tokens_per_s": round(tokens / dt, 1), "ms_per_step": round(dt / steps * 1e3, 4),
+                     "admissions": admitted[0]}
+        loop.close()
+        del loop
+        torch.cuda.empty_cache()
+    return {
+        "workload": "continuous-batching decode loop: 64 slots, 16 layers, 24/4 heads, d 256, "
+                    "bs 16, P 1024, prompts log-uniform [16, 8192], generation uniform [16, 128]",
+        "steps": steps, **res,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -356,6 +424,7 @@ def main():
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)
+        result["loop"] = loop_leg(args.seed, 5 * args.prefill_reps, dev)
     if args.cpu_seconds > 0 and W == "mixed":
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     if args.copy_calibration:

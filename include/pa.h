@@ -272,6 +272,26 @@ int32_t pa_alloc_take_copies(pa_alloc *a, int32_t *pairs_out, int32_t max_pairs)
 /* Number of sequences holding block (0 = free), or -1 if out of range. */
 int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block);
 
+/* One step of an iteration-level decode loop ([W2] s.3 "Continuous
+ * Batching": every iteration each running sequence gets its next token, and
+ * finished ones leave at once), in one call: append num_tokens[i] tokens to
+ * seq_ids[i] for i < n (as pa_alloc_append, copy on write included), then
+ * write the block-table rows and context lengths of the n sequences (as
+ * pa_alloc_block_table).
+ *  seq_ids    [host] int64 [n], distinct
+ *  num_tokens [host] int32 [n], >= 0
+ *  slots_out  [host] int64 [sum num_tokens]: the new tokens' slots, sequence
+ *             by sequence in the order of seq_ids (NULL allowed if the sum is 0)
+ *  table_out  [host] int32 [n][max_blocks], unused entries -1
+ *  lens_out   [host] int32 [n] or NULL
+ * All or nothing: PA_ENOMEM if the step needs more blocks (growth plus
+ * copy-on-write replacements) than are free, PA_EINVAL for a sequence listed
+ * twice or one that would hold more than max_blocks blocks; nothing changes
+ * then. Copies are queued as by pa_alloc_append. */
+pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const int32_t *num_tokens, int32_t n,
+                        int64_t *slots_out, int32_t max_blocks, int32_t *table_out,
+                        int32_t *lens_out);
+
 /* Free blocks in the pool; -1 if a is NULL. */
 int32_t pa_alloc_num_free(const pa_alloc *a);
 

@@ -45,6 +45,7 @@ SIGNATURES = {
     "pa_alloc_fork": (_st, [_p, _i64, _i64]),
     "pa_alloc_take_copies": (_i32, [_p, _p, _i32]),
     "pa_alloc_block_refs": (_i32, [_p, _i32]),
+    "pa_alloc_step": (_st, [_p, _p, _p, _i32, _p, _i32, _p, _p]),
 }
 
 _LIB = None

@@ -243,6 +243,25 @@ class BlockAllocator:
     def block_refs(self, block):
         return int(lib().pa_alloc_block_refs(self._h, int(block)))
 
+    def step(self, seq_ids, num_tokens, max_blocks, slots_out=None, table_out=None,
+             lens_out=None):
+        """Append num_tokens[i] tokens to seq_ids[i] and export the table rows
+        in one native call; returns (slots, table, lens). Output arrays may be
+        passed in (e.g. pinned host buffers) to avoid allocations."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        nt = np.ascontiguousarray(num_tokens, dtype=np.int32)
+        n = len(ids)
+        total = int(nt.sum()) if n else 0
+        slots = slots_out if slots_out is not None else np.empty(total, dtype=np.int64)
+        table = table_out if table_out is not None else np.empty((n, max_blocks), dtype=np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, dtype=np.int32)
+        check(lib().pa_alloc_step(self._h, ids.ctypes.data if n else None,
+                                  nt.ctypes.data if n else None, n,
+                                  slots.ctypes.data if total else None, int(max_blocks),
+                                  table.ctypes.data if n else None,
+                                  lens.ctypes.data if n else None))
+        return slots[:total], table[:n], lens[:n]
+
     def block_table(self, seq_ids, max_blocks):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         table = np.empty((len(ids), max_blocks), dtype=np.int32)

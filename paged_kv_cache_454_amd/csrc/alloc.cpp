@@ -218,3 +218,58 @@ extern "C" pa_status pa_alloc_block_table(const pa_alloc *a, const int64_t *seq_
   }
   return PA_OK;
 }
+
+extern "C" pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const int32_t *num_tokens,
+                                   int32_t n, int64_t *slots_out, int32_t max_blocks,
+                                   int32_t *table_out, int32_t *lens_out) {
+  pa::clear_error();
+  if (!a || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !num_tokens || !table_out)))
+    return pa::fail(PA_EINVAL, "pa_alloc_step: bad arguments");
+  // Check the whole step first so that it is all or nothing: blocks needed
+  // (growth plus copy-on-write replacements) against the free queue, table
+  // widths, and no sequence listed twice.
+  int64_t need = 0, total = 0;
+  try {
+    std::unordered_map<int64_t, int> seen;
+    std::unordered_map<int32_t, int> left;  // holders a shared last block loses this step
+    seen.reserve((size_t)n * 2);
+    for (int32_t i = 0; i < n; ++i) {
+      if (num_tokens[i] < 0)
+        return pa::fail(PA_EINVAL, "pa_alloc_step: num_tokens[%d]=%d", i, num_tokens[i]);
+      if (seen[seq_ids[i]]++)
+        return pa::fail(PA_EINVAL, "pa_alloc_step: sequence %lld listed twice",
+                        (long long)seq_ids[i]);
+      auto it = a->seqs.find(seq_ids[i]);
+      const int64_t held = it == a->seqs.end() ? 0 : it->second.len;
+      const int64_t have = it == a->seqs.end() ? 0 : (int64_t)it->second.blocks.size();
+      const int64_t want = (held + num_tokens[i] + a->block_size - 1) / a->block_size;
+      if (want > max_blocks)
+        return pa::fail(PA_EINVAL, "pa_alloc_step: sequence %lld would hold %lld blocks > %d",
+                        (long long)seq_ids[i], (long long)want, max_blocks);
+      bool cow = false;
+      if (num_tokens[i] > 0 && held % a->block_size != 0) {
+        const int32_t last = it->second.blocks.back();
+        // Earlier sequences of this step that copied away from the same
+        // block leave fewer holders; the last one writes in place.
+        cow = a->refs[last] - left[last] > 1;
+        if (cow) ++left[last];
+      }
+      need += want - have + cow;
+      total += num_tokens[i];
+    }
+  } catch (...) {
+    return pa::fail(PA_ENOMEM, "pa_alloc_step: host allocation failed");
+  }
+  if (need > a->count)
+    return pa::fail(PA_ENOMEM, "pa_alloc_step: the step needs %lld blocks, %lld free",
+                    (long long)need, (long long)a->count);
+  if (total > 0 && !slots_out) return pa::fail(PA_EINVAL, "pa_alloc_step: slots_out is NULL");
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pa_status st = pa_alloc_append(a, seq_ids[i], num_tokens[i],
+                                         num_tokens[i] > 0 ? slots_out + off : nullptr);
+    if (st != PA_OK) return st;  // host allocation failure only (capacity was checked)
+    off += num_tokens[i];
+  }
+  return pa_alloc_block_table(a, seq_ids, n, max_blocks, table_out, lens_out);
+}

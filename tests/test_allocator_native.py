@@ -158,3 +158,74 @@ def test_fork_errors_and_copy_queue():
     assert a.num_free() == 6 and a.block_refs(0) == 1           # block 0 still held by 2
     a.free(2)
     assert a.num_free() == 8
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_step_matches_oracle_appends(seed):
+    """pa_alloc_step equals the same appends made one by one on the oracle's
+    model followed by its block table, copies included; a step that does not
+    fit changes nothing."""
+    rng = random.Random(200 + seed)
+    nb, bs = rng.choice([(64, 4), (200, 16), (48, 5)])
+    a = BlockAllocator(nb, bs)
+    m = model.BlockAllocatorModel(nb, bs)
+    live = []   # sequences the allocator knows
+    for it in range(120):
+        if live and rng.random() < 0.2:
+            parent = rng.choice(live)
+            child = 1000 + it
+            a.fork(parent, child)
+            m.fork(parent, child)
+            live.append(child)
+        if live and rng.random() < 0.15:
+            sid = live.pop(rng.randrange(len(live)))
+            a.free(sid)
+            m.free(sid)
+        ids = rng.sample(live, k=rng.randint(1, len(live))) if live else []
+        nt = [rng.randint(0, 2 * bs) if rng.random() < 0.3 else 1 for _ in ids]
+        if rng.random() < 0.3 or not live:
+            ids.append(it)                                      # a new sequence joins
+            nt.append(rng.randint(1, 3 * bs))
+        maxb = 64
+        before = (m.num_free(), {k: list(v) for k, v in m.tables.items()})
+        try:
+            want_slots = []
+            for sid, n in zip(ids, nt):
+                want_slots += m.append(sid, n)
+            ok = True
+        except model.OutOfBlocks:
+            ok = False
+        if not ok:
+            # the model applied part of the step; rebuild it from the native state instead
+            with pytest.raises(PAError) as e:
+                a.step(ids, nt, maxb)
+            assert e.value.status == PA_ENOMEM
+            assert a.num_free() == before[0]
+            return
+        slots, table, lens = a.step(ids, nt, maxb)
+        live += [sid for sid in ids if sid not in live]
+        assert list(slots) == want_slots
+        t_m, l_m = m.block_table(ids, maxb)
+        assert np.array_equal(table, np.array(t_m, dtype=np.int32)) and list(lens) == l_m
+        assert [tuple(p) for p in a.take_copies().tolist()] == m.take_copies()
+        assert a.num_free() == m.num_free()
+
+
+def test_step_errors():
+    a = BlockAllocator(8, 4)
+    with pytest.raises(PAError) as e:
+        a.step([1, 1], [1, 1], 4)                               # listed twice
+    assert e.value.status == PA_EINVAL
+    with pytest.raises(PAError) as e:
+        a.step([1], [20], 4)                                    # more than max_blocks
+    assert e.value.status == PA_EINVAL and a.seq_len(1) == -1
+    a.step([1], [6], 4)
+    a.fork(1, 2)
+    a.fork(1, 3)
+    # three holders of a half-full block: two copies, the last writes in place
+    slots, table, lens = a.step([1, 2, 3], [1, 1, 1], 4)
+    assert a.take_copies().tolist() == [[1, 2], [1, 3]] and list(lens) == [7, 7, 7]
+    assert a.num_free() == 4
+    with pytest.raises(PAError) as e:
+        a.step([1, 2, 3], [8, 4, 8], 4)                          # needs 2+1+2 blocks, 4 free
+    assert e.value.status == PA_ENOMEM and a.num_free() == 4 and a.seq_len(1) == 7
