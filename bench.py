@@ -73,6 +73,8 @@ def parse():
                          "between those counters and bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
+    ap.add_argument("--loop-steps", type=int, default=50,
+                    help="timed iterations of the continuous-batching loop leg (0 skips it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
                     help="timed repetitions of the side legs, chunked prefill and "
                          "copy-on-write block copies (0 skips them)")
@@ -424,7 +426,8 @@ def main():
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)
-        result["loop"] = loop_leg(args.seed, 5 * args.prefill_reps, dev)
+    if args.loop_steps > 0:
+        result["loop"] = loop_leg(args.seed, args.loop_steps, dev)
     if args.cpu_seconds > 0 and W == "mixed":
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     if args.copy_calibration:
