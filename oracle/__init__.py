@@ -26,6 +26,10 @@ Modules:
   contiguous and paged policies (pinned by the pages' printed numbers).
 * ``allocator``  - a model of the on-demand block allocator with a FIFO free
   list (pinned by the worked example and the pages' stated invariants).
+* ``fp8``        - E4M3 codes (a stated choice; the pages define no quantised
+  cache), the quantising cache write and decode over the dequantised cache
+  (pinned by known codes, the full code table, torch's float8_e4m3fn
+  conversion and tie cases).
 * ``attention``  - the slot-mapped cache write, logical reassembly of a paged
   cache, dense softmax decode attention, split-context partitions and their
   log-sum-exp merge, and causal chunked prefill (pinned by brute force,
@@ -35,4 +39,4 @@ Parity status: every function above has at least one pin that does not reuse
 its own formula; none is "parity unpinned".
 """
 
-from . import accounting, allocator, attention  # noqa: F401
+from . import accounting, allocator, attention, fp8  # noqa: F401

@@ -518,9 +518,100 @@ def pin_copy_blocks(attn):
                     assert v2[b, h, r, c] == vc[src, h, r, c]
 
 
+# -------------------------------------------------------------- fp8
+
+def pin_fp8_codes(fp8):
+    """E4M3FN codes from the format's definition, independent of the
+    encoder's search: known values, every code back to itself, torch's
+    float8_e4m3fn conversion on in-range values, ties to even, saturation."""
+    import torch
+    known = [(0.0, 0x00), (-0.0, 0x80), (1.0, 0x38), (-2.0, 0xC0), (0.5, 0x30), (448.0, 0x7E),
+             (-448.0, 0xFE), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01), (7 * 2.0 ** -9, 0x07),
+             (1.75, 0x3E), (240.0, 0x77), (0.015625 * 1.875, 0x0F)]   # pairs: 0.0 == -0.0
+    for x, c in known:
+        assert int(fp8.encode_e4m3([x])[0]) == c, (x, c)
+        assert fp8.decode_e4m3([c])[0] == x or (x == 0 and fp8.decode_e4m3([c])[0] == 0)
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = fp8.decode_e4m3(codes)
+    assert list(fp8.encode_e4m3(vals)) == codes                 # every code maps back
+    assert np.isnan(fp8.decode_e4m3([0x7F, 0xFF])).all()
+    assert int(fp8.encode_e4m3([np.nan])[0]) == 0x7F
+    pos = np.sort(vals[vals > 0])
+    assert pos[-1] == 448.0 and pos[0] == 2.0 ** -9 and len(pos) == 126
+    # torch's conversion (round to nearest even) on finite in-range values
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 0.1, 3.0, 100.0)])
+    x = x[np.abs(x) < 448.0].astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.encode_e4m3(x.astype(np.float64)), ref)
+    # ties between neighbouring codes go to the even code
+    for lo in (0x38, 0x39, 0x01, 0x10, 0x7C):
+        a, b = fp8.decode_e4m3([lo, lo + 1])
+        want = lo if lo % 2 == 0 else lo + 1
+        assert int(fp8.encode_e4m3([(a + b) / 2])[0]) == want
+    # saturation (a stated choice): beyond 448 stays at the largest finite code
+    assert list(fp8.encode_e4m3([460.0, 500.0, 1e9, -1e9])) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def pin_fp8_cache(fp8):
+    """The quantising cache write stores torch's codes of the fp32 quotients
+    at the written slots (and nothing else); decode over a cache whose values
+    are all exactly representable equals the unquantised decode."""
+    import torch
+    rng = np.random.default_rng(29)
+    nb, hkv, bs, d = 6, 2, 4, 8
+    kc = np.zeros((nb, hkv, bs, d), np.uint8)
+    vc = np.zeros((nb, hkv, bs, d), np.uint8)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    slots = np.array([3, 9, -1, 22, 0])
+    ks, vs = 0.05, 0.02
+    k2, v2 = fp8.cache_write(kc, vc, key, val, slots, bs, ks, vs)
+    for i, sl in enumerate(slots.tolist()):
+        if sl < 0:
+            continue
+        qk = (torch.from_numpy(key[i]) / torch.tensor(ks, dtype=torch.float32))
+        qv = (torch.from_numpy(val[i]) / torch.tensor(vs, dtype=torch.float32))
+        assert np.array_equal(k2[sl // bs, :, sl % bs], qk.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        assert np.array_equal(v2[sl // bs, :, sl % bs], qv.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert int((k2 != 0).sum()) <= 4 * hkv * d and np.array_equal(k2[1], kc[1])  # block 1 unwritten
+    # values on the E4M3 grid times the scale survive exactly: fp8 decode = plain decode
+    codes_k = rng.integers(0, 0x7E, size=(nb, hkv, bs, d)).astype(np.uint8)
+    codes_v = rng.integers(0, 0x7E, size=(nb, hkv, bs, d)).astype(np.uint8)
+    q = rng.standard_normal((2, 4, d))
+    tables = np.array([[0, 3, -1], [5, 1, 2]])
+    lens = np.array([7, 12])
+    got = fp8.decode(q, codes_k, codes_v, tables, lens, bs, 0.3, 0.25, 2.0)
+    want = attention_decode_ref(q, fp8.decode_e4m3(codes_k) * 0.25, fp8.decode_e4m3(codes_v) * 2.0,
+                                tables, lens, bs, 0.3)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def attention_decode_ref(q, kc, vc, tables, lens, bs, scale):
+    """Brute-force decode (loops), for the fp8 pin."""
+    out = np.zeros(q.shape)
+    hq, hkv = q.shape[1], kc.shape[1]
+    for s in range(q.shape[0]):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            z = []
+            for t in range(int(lens[s])):
+                blk = int(tables[s][t // bs])
+                z.append(scale * float(np.dot(q[s, h], kc[blk, g, t % bs])))
+            zmax = max(z)
+            w = [np.exp(v - zmax) for v in z]
+            acc = np.zeros(q.shape[2])
+            for t, wt in enumerate(w):
+                blk = int(tables[s][t // bs])
+                acc += wt * vc[blk, g, t % bs]
+            out[s, h] = acc / sum(w)
+    return out
+
+
 ATTENTION_PINS = [pin_cache_write, pin_decode_bruteforce, pin_decode_vs_library,
                   pin_decode_special_cases, pin_permutation_invariance, pin_partitions,
                   pin_prefill, pin_copy_blocks]
 ACCOUNTING_PINS = [pin_kv_size, pin_worked_example_accounting]
+FP8_PINS = [pin_fp8_codes, pin_fp8_cache]
 ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants, pin_cow_contents,
                   pin_cow_counts]

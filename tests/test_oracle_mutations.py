@@ -63,8 +63,25 @@ MUTATIONS = [
      "want = (held + num_tokens) // self.block_size + 1"),
 ]
 
+MUTATIONS += [
+    ("fp8", "val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))",
+     "val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 8))"),
+    ("fp8", "            m = int(np.rint(a / 2.0 ** -9))     # exact quotient, ties to even",
+     "            m = int(np.floor(a / 2.0 ** -9))"),
+    ("fp8", "        m = int(np.rint((a / 2.0 ** e - 1.0) * 8.0))",
+     "        m = int(np.floor((a / 2.0 ** e - 1.0) * 8.0 + 0.5))"),
+    ("fp8", "        if a >= E4M3_MAX:\n            flat_o[i] = s | 0x7E",
+     "        if a >= E4M3_MAX:\n            flat_o[i] = s | 0x7F"),
+    ("fp8", "        flat_o[i] = s | ((e + 7) << 3) | m", "        flat_o[i] = s | ((e + 7) << 3) | (m ^ 1)"),
+    ("fp8", "    q = np.asarray(x, dtype=np.float32) / np.float32(scale)",
+     "    q = np.asarray(x, dtype=np.float32) * np.float32(scale)"),
+    ("fp8", "    return decode_e4m3(codes) * float(np.float32(scale))",
+     "    return decode_e4m3(codes)"),
+    ("fp8", "        s = 0x80 if np.signbit(x) else 0", "        s = 0x80 if x < 0 else 0"),
+]
+
 PINS = {"attention": P.ATTENTION_PINS, "accounting": P.ACCOUNTING_PINS,
-        "allocator": P.ALLOCATOR_PINS}
+        "allocator": P.ALLOCATOR_PINS, "fp8": P.FP8_PINS}
 
 
 def _mutant(modname, old, new):
@@ -73,6 +90,7 @@ def _mutant(modname, old, new):
         src = f.read()
     assert src.count(old) == 1, f"mutation anchor not unique in {modname}: {old!r}"
     mod = types.ModuleType("mutant_" + modname)
+    mod.__package__ = "oracle"   # relative imports resolve to the real oracle modules
     exec(compile(src.replace(old, new), path, "exec"), mod.__dict__)
     return mod
 

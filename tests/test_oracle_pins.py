@@ -2,7 +2,7 @@
 
 import pytest
 
-from oracle import accounting, allocator, attention
+from oracle import accounting, allocator, attention, fp8
 from tests import oracle_pins as P
 
 
@@ -19,3 +19,8 @@ def test_allocator_pin(pin):
 @pytest.mark.parametrize("pin", P.ATTENTION_PINS, ids=lambda f: f.__name__)
 def test_attention_pin(pin):
     pin(attention)
+
+
+@pytest.mark.parametrize("pin", P.FP8_PINS, ids=lambda f: f.__name__)
+def test_fp8_pin(pin):
+    pin(fp8)
