@@ -73,6 +73,10 @@ def parse():
                          "between those counters and bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
+    ap.add_argument("--fp8", type=int, default=1,
+                    help="also time the step over FP8 (E4M3FN) pools (0: skip)")
+    ap.add_argument("--fp8-partition-size", type=int, default=None,
+                    help="partition size of the FP8 leg (default: the BF16 one)")
     ap.add_argument("--loop-steps", type=int, default=50,
                     help="timed iterations of the continuous-batching loop leg (0 skips it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
@@ -319,6 +323,86 @@ def loop_leg(seed, steps, dev):
     }
 
 
+FP8_SCALES = (0.0375, 0.021)   # k_scale, v_scale of the FP8 pools (N(0,1) data)
+
+
+def fp8_leg(layers, meta, P, steps, warmup, dev):
+    """The same decode step over FP8 (E4M3FN) pools: each layer's BF16 pools
+    are converted to codes of value / scale before timing (input
+    preparation); one step = per layer the quantising write of the step's new
+    K/V (pa_reshape_and_cache_fp8), pa_decode_partitioned_fp8 and pa_reduce."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    ks, vs = FP8_SCALES
+
+    def codes(x, sc):
+        return (x.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    pools = [(codes(L["key_cache"], ks), codes(L["value_cache"], vs)) for L in layers]
+    torch.cuda.synchronize()
+    lens = meta["lens"]
+    S = len(lens)
+    hq, d = layers[0]["query"].shape[1], layers[0]["query"].shape[2]
+    hkv = pools[0][0].shape[1]
+    max_parts = max(1, math.ceil(int(lens.max()) / P))
+    po = torch.empty((S, hq, max_parts, d), dtype=torch.float32, device=dev)
+    pm = torch.empty((S, hq, max_parts), dtype=torch.float32, device=dev)
+    ps = torch.empty((S, hq, max_parts), dtype=torch.float32, device=dev)
+    outs = [torch.empty((S, hq, d), dtype=torch.float32, device=dev) for _ in layers]
+    bt, cl, sm = meta["block_tables"], meta["context_lens"], meta["slot_mapping"]
+    scale = meta["scale"]
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        for li, L in enumerate(layers):
+            kc, vc = pools[li]
+            pa.pa_reshape_and_cache_fp8(L["key"], L["value"], kc, vc, sm, ks, vs, stream=stream)
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pa.pa_decode_partitioned_fp8(po, pm, ps, L["query"], kc, vc, bt, cl, scale, ks, vs, P,
+                                         stream=stream)
+            if record:
+                e1.record(stream)
+                ev.append((e0, e1))
+            pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step(False)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+    for _ in range(max(3, min(steps, 20))):
+        step(True)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    kv_bytes_layer = int(lens.sum()) * hkv * d * 2      # one byte per element, K and V
+    k_gbs = kv_bytes_layer / (kern_ms * 1e-3) / 1e9
+    del pools, po, pm, ps, outs
+    torch.cuda.empty_cache()
+    return {
+        "what": "the decode step over FP8 E4M3FN pools (scales k 0.0375, v 0.021): per layer "
+                "pa_reshape_and_cache_fp8 + pa_decode_partitioned_fp8 + pa_reduce",
+        "ms_per_step": round(ms_step, 5),
+        "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "kv_gbs_effective": round(kv_bytes_layer * len(layers) / (ms_step * 1e-3) / 1e9, 2),
+        "partition_size": P,
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned_fp8",
+                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": kv_bytes_layer},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -421,8 +505,14 @@ def main():
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
+    if args.fp8:
+        del po, pm, ps, outs
+        result["fp8"] = fp8_leg(layers, meta, args.fp8_partition_size or P, args.steps,
+                                args.warmup, dev)
     if args.prefill_reps > 0:
-        del layers, po, pm, ps, outs
+        del layers
+        if not args.fp8:
+            del po, pm, ps, outs
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)

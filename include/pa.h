@@ -64,7 +64,9 @@ typedef enum pa_status {
   PA_ENOTFOUND = 5      /* allocator: unknown sequence id                    */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8_E4M3: one-byte OCP E4M3FN codes (pools of the *_fp8 entry points
+ * and pa_copy_blocks only; see pa_reshape_and_cache_fp8). */
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Message describing the last non-OK status returned on this thread
  * ("" if none). The string stays valid until the next call on the thread. */
@@ -99,7 +101,8 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
  * num_kv_heads x block_size rows of block src are copied to block dst, in
  * both pools.
  *  key_cache,
- *  value_cache  [device] kv_dtype pools (layout above), updated in place
+ *  value_cache  [device] kv_dtype pools (layout above), updated in place;
+ *               kv_dtype PA_F32, PA_BF16 or PA_FP8_E4M3
  *  block_pairs  [device] int32 [num_pairs][2] = (src, dst)
  * A pair with an id outside [0, num_blocks), or with src == dst, is skipped.
  * Destinations must be distinct and never the source of another pair (the
@@ -221,6 +224,64 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
                            pa_dtype kv_dtype, pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * FP8 KV cache. The pools hold one-byte E4M3FN codes (OCP 8-bit floating
+ * point: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, values
+ * down to 2^-9, largest finite magnitude 448, no infinities, 0x7F / 0xFF
+ * NaN), with one scale per pool: a code c with scale s stands for
+ * value(c) * s. Halving the bytes per element halves both the cache's size
+ * and the bytes decode streams ([P3] KV-cache section: the cache size is
+ * linear in the bytes per element; [P2] s.1: decode is bound by memory
+ * traffic). The pages fix no quantised format; this one is the library's
+ * choice. Pool layout and the block table are as above, element size 1.
+ *
+ * pa_reshape_and_cache_fp8 - the slot-mapped write of pa_reshape_and_cache,
+ * quantising on the way: the code stored for element x of key (value) is
+ * the E4M3 value nearest to the fp32 quotient x / k_scale (x / v_scale),
+ * computed as a correctly rounded fp32 division; ties round to even,
+ * magnitudes of 448 and above (and infinities) become +-448, NaN becomes
+ * 0x7F.
+ *  key, value   [device] in_dtype (PA_F32 or PA_BF16) [num_tokens][num_kv_heads][head_dim]
+ *  key_cache,
+ *  value_cache  [device] uint8 code pools, updated in place
+ *  slot_mapping [device] int64 [num_tokens] (negative: token skipped)
+ *  k_scale, v_scale  finite, > 0 (PA_EINVAL otherwise)
+ * num_tokens == 0 is a no-op. head_dim in [1, 1024].
+ */
+pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *key_cache,
+                                   uint8_t *value_cache, const int64_t *slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, pa_dtype in_dtype,
+                                   float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * pa_decode_fp8 / pa_decode_partitioned_fp8 - pa_decode and
+ * pa_decode_partitioned over FP8 pools: attention over the dequantised
+ * cache, K_t = value(code) * k_scale and V_t = value(code) * v_scale.
+ * query is BF16 [num_seqs][num_q_heads][head_dim]; the other arguments,
+ * outputs, workspace layout and error behaviour are those of the BF16 entry
+ * points (pa_reduce merges the partitions). Codes widen to BF16 exactly;
+ * the K scale is applied to the logits and the V scale to the outputs, in
+ * fp32. Supported shapes as pa_decode (head_dim 64/128/256, groups <= 8);
+ * head_dim 256 with block_size a multiple of 16 takes the persistent kernel.
+ */
+pa_status pa_decode_fp8(void *out, const void *query, const uint8_t *key_cache,
+                        const uint8_t *value_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                        float k_scale, float v_scale, pa_dtype out_dtype, hipStream_t stream);
+
+pa_status pa_decode_partitioned_fp8(float *part_out, float *part_max, float *part_sum,
+                                    const void *query, const uint8_t *key_cache,
+                                    const uint8_t *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, float scale, float k_scale,
+                                    float v_scale, int32_t partition_size, int32_t max_parts,
+                                    hipStream_t stream);
 
 /*
  * Host block allocator ([P2] s.2 "On-Demand Allocation": blocks are handed

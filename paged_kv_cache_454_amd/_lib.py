@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ENOMEM, PA_EHIP, PA_ENOTFOUND = range(6)
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_ENOMEM",
                 4: "PA_EHIP", 5: "PA_ENOTFOUND"}
 
@@ -27,6 +27,12 @@ SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_st, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st, _p]),
     "pa_copy_blocks": (_st, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st, _p]),
+    "pa_reshape_and_cache_fp8": (_st, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st,
+                                       _f32, _f32, _p]),
+    "pa_decode_fp8": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                            _f32, _f32, _f32, _st, _p]),
+    "pa_decode_partitioned_fp8": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _f32, _f32, _f32, _i32, _i32, _p]),
     "pa_decode": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _st, _st, _p]),
     "pa_partition_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),

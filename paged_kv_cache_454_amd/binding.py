@@ -12,9 +12,11 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_F32, PAError, check, lib  # noqa: F401
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PAError, check, lib  # noqa: F401
 
 _DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+# FP8 pools: E4M3FN codes, as uint8 or as torch's float8_e4m3fn.
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _dtype(t, what):
@@ -78,16 +80,42 @@ def pa_copy_blocks(key_cache, value_cache, block_pairs, stream=None):
     if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be int32 [num_pairs][2]")
     n = block_pairs.shape[0]
+    dt = PA_FP8_E4M3 if key_cache.dtype in _FP8 else _dtype(key_cache, "pools")
     check(lib().pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
                                _dev(block_pairs, "block_pairs", torch.int32), n, hkv, d, bs,
-                               num_blocks, _dtype(key_cache, "pools"), _stream(stream)))
+                               num_blocks, dt, _stream(stream)))
 
 
-def _attn_common(query, key_cache, value_cache, block_tables, context_lens, rows_name):
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                             stream=None):
+    """Quantising write: the E4M3 codes of key / k_scale and value / v_scale
+    (key/value float32 or bfloat16 [num_tokens][H_KV][d]) go into the uint8
+    (or float8_e4m3fn) pools at slot_mapping."""
+    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    if key_cache.dtype not in _FP8:
+        raise ValueError("pools must be uint8 or float8_e4m3fn")
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens][num_kv_heads][head_dim] matching the pools")
+    if key.dtype != value.dtype:
+        raise ValueError("key and value must share a dtype")
+    n = key.shape[0]
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != n:
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    args = [_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64)]
+    check(lib().pa_reshape_and_cache_fp8(*args, n, hkv, d, bs, num_blocks, _dtype(key, "key"),
+                                         float(k_scale), float(v_scale), _stream(stream)))
+
+
+def _attn_common(query, key_cache, value_cache, block_tables, context_lens, rows_name,
+                 fp8=False):
     num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
     if query.dim() != 3 or query.shape[2] != d:
         raise ValueError(f"query must be [{rows_name}][num_q_heads][{d}]")
-    if query.dtype != key_cache.dtype:
+    if fp8:
+        if key_cache.dtype not in _FP8 or query.dtype != torch.bfloat16:
+            raise ValueError("FP8 decode takes uint8 / float8_e4m3fn pools and a bfloat16 query")
+    elif query.dtype != key_cache.dtype:
         raise ValueError("query dtype must match the pools")
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be int32 [num_seqs][max_blocks_per_seq]")
@@ -138,6 +166,45 @@ def pa_decode_partitioned(part_out, part_max, part_sum, query, key_cache, value_
         _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
         context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
         float(scale), int(partition_size), max_parts, _dtype(key_cache, "pools"),
+        _stream(stream)))
+
+
+def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                  k_scale, v_scale, stream=None):
+    """pa_decode over FP8 pools (codes times k_scale / v_scale); bfloat16 query."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs", fp8=True)
+    if query.shape[0] != num_seqs or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("query/out must be [num_seqs][num_q_heads][head_dim]")
+    hq = query.shape[1]
+    check(lib().pa_decode_fp8(_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+                              _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+                              context_lens.data_ptr(), num_seqs, hq, hkv, d, bs,
+                              block_tables.shape[1], num_blocks, float(scale), float(k_scale),
+                              float(v_scale), _dtype(out, "out"), _stream(stream)))
+
+
+def pa_decode_partitioned_fp8(part_out, part_max, part_sum, query, key_cache, value_cache,
+                              block_tables, context_lens, scale, k_scale, v_scale,
+                              partition_size, stream=None):
+    """pa_decode_partitioned over FP8 pools; pa_reduce merges the partitions."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs", fp8=True)
+    hq = query.shape[1]
+    if query.shape[0] != num_seqs:
+        raise ValueError("query must be [num_seqs][num_q_heads][head_dim]")
+    if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (num_seqs, hq) or part_out.shape[3] != d:
+        raise ValueError("part_out must be float32 [num_seqs][num_q_heads][max_parts][head_dim]")
+    max_parts = part_out.shape[2]
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (num_seqs, hq, max_parts):
+            raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
+    check(lib().pa_decode_partitioned_fp8(
+        _dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
+        _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
+        float(scale), float(k_scale), float(v_scale), int(partition_size), max_parts,
         _stream(stream)))
 
 

@@ -70,7 +70,11 @@ __device__ __forceinline__ RowWork row_work(const DecodeParams &p, int vrow) {
 
 template <typename KV, int HEAD_DIM, int MAXG, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p) {
-  constexpr int VEC = Widen<KV>::N;
+  using Piece = KvPiece<KV>;
+  using QT = typename Piece::Q;
+  constexpr int VEC = Piece::N;
+  static_assert(Widen<QT>::N == VEC, "query and K/V pieces must cover the same channels");
+  constexpr bool F8 = sizeof(KV) == 1;
   constexpr int LPR = HEAD_DIM / VEC;  // lanes per token row
   constexpr int RPL = 64 / LPR;        // token rows per wavefront load
   static_assert(HEAD_DIM % VEC == 0 && LPR <= 64 && 64 % LPR == 0, "unsupported shape");
@@ -113,8 +117,8 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
 #pragma unroll
   for (int h = 0; h < MAXG; ++h) {
     if (h < group) {
-      const KV *qp = reinterpret_cast<const KV *>(p.query) + (qrow + h) * HEAD_DIM + c * VEC;
-      Widen<KV>::apply(load16(qp), q[h]);
+      const QT *qp = reinterpret_cast<const QT *>(p.query) + (qrow + h) * HEAD_DIM + c * VEC;
+      Widen<QT>::apply(load16(qp), q[h]);
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) q[h][v] = 0.f;
@@ -130,7 +134,10 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
     for (int v = 0; v < VEC; ++v) acc[h][v] = 0.f;
   }
 
-  const float sl2 = p.scale * kLog2e;
+  // An FP8 cache holds K / k_scale: the K scale folds into the logit scale,
+  // the V scale into the final outputs.
+  const float sl2 = p.scale * kLog2e * (F8 ? p.k_scale : 1.f);
+  const float vsc = F8 ? p.v_scale : 1.f;
   const int bs = p.block_size;
   const int32_t *table = p.block_tables + (int64_t)w.seq * p.max_blocks_per_seq;
   const int64_t head_stride = (int64_t)bs * HEAD_DIM;
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
     }
     float kf[VEC], vf[VEC];
     if (valid) {
-      Widen<KV>::apply(load16(kbase + off), kf);
-      Widen<KV>::apply(load16(vbase + off), vf);
+      Piece::load(kbase + off, kf);
+      Piece::load(vbase + off, vf);
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) kf[v] = vf[v] = 0.f;
@@ -227,11 +234,11 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
       A += sm_acc[i][h][ch] * f;
     }
     if (p.partition_size == 0) {
-      const float o = bad ? nan : (L > 0.f ? A / L : 0.f);
+      const float o = bad ? nan : (L > 0.f ? A / L * vsc : 0.f);
       store_out(p.out, (qrow + h) * HEAD_DIM + ch, o, p.out_bf16);
     } else {
       const int64_t pidx = (qrow + h) * p.max_parts + part;
-      p.part_out[pidx * HEAD_DIM + ch] = bad ? nan : A / L;
+      p.part_out[pidx * HEAD_DIM + ch] = bad ? nan : A / L * vsc;
       if (ch == 0) {
         p.part_max[pidx] = bad ? nan : M * kLn2;
         p.part_sum[pidx] = bad ? nan : L;
@@ -279,7 +286,9 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream) {
   if (grid > 0x7fffffff) return fail(PA_EUNSUPPORTED, "decode: grid of %lld workgroups", (long long)grid);
   if (launch_decode_persistent(p, stream)) return check_launch("decode");
   if (launch_decode_tiled(p, (unsigned)grid, stream)) return check_launch("decode");
-  if (p.kv_bf16)
+  if (p.kv_fp8)
+    launch_generic_d<fp8_t>(p, group, (unsigned)grid, stream);
+  else if (p.kv_bf16)
     launch_generic_d<bf16_t>(p, group, (unsigned)grid, stream);
   else
     launch_generic_d<float>(p, group, (unsigned)grid, stream);

@@ -16,6 +16,12 @@ pa_status launch_cache_write(const void *key, const void *value, void *key_cache
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int elem_bytes, hipStream_t stream);
 
+pa_status launch_cache_write_fp8(const void *key, const void *value, uint8_t *key_cache,
+                                 uint8_t *value_cache, const int64_t *slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, bool in_bf16,
+                                 float k_scale, float v_scale, hipStream_t stream);
+
 // Arguments of the decode kernels (single pass when partition_size == 0).
 struct DecodeParams {
   const void *query;
@@ -42,6 +48,9 @@ struct DecodeParams {
   int32_t max_parts;       // 1 for single pass
   int32_t kv_bf16;
   int32_t out_bf16;
+  int32_t kv_fp8;   // E4M3FN code pools, BF16 queries; logits scale by k_scale,
+  float k_scale;    // outputs by v_scale (used only when kv_fp8)
+  float v_scale;
 };
 
 pa_status launch_decode(const DecodeParams &p, hipStream_t stream);

@@ -7,7 +7,14 @@
 namespace {
 
 bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_BF16; }
-int dtype_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
+int dtype_bytes(pa_dtype t) { return t == PA_FP8_E4M3 ? 1 : t == PA_BF16 ? 2 : 4; }
+
+pa_status check_fp8_scales(const char *fn, float k_scale, float v_scale) {
+  if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return pa::fail(PA_EINVAL, "%s: k_scale=%g v_scale=%g must be finite and > 0", fn,
+                    (double)k_scale, (double)v_scale);
+  return PA_OK;
+}
 
 // Shared checks of the paged-attention shapes.
 pa_status check_attention_shape(const char *fn, int32_t num_seqs, int32_t num_q_heads,
@@ -61,6 +68,31 @@ extern "C" pa_status pa_reshape_and_cache(const void *key, const void *value, vo
                                 dtype_bytes(kv_dtype), stream);
 }
 
+extern "C" pa_status pa_reshape_and_cache_fp8(const void *key, const void *value,
+                                              uint8_t *key_cache, uint8_t *value_cache,
+                                              const int64_t *slot_mapping, int32_t num_tokens,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t num_blocks,
+                                              pa_dtype in_dtype, float k_scale, float v_scale,
+                                              hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_reshape_and_cache_fp8";
+  if (num_tokens < 0) return pa::fail(PA_EINVAL, "%s: num_tokens=%d < 0", fn, num_tokens);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa::fail(PA_EINVAL, "%s: num_kv_heads=%d head_dim=%d block_size=%d num_blocks=%d", fn,
+                    num_kv_heads, head_dim, block_size, num_blocks);
+  if (head_dim > 1024) return pa::fail(PA_EUNSUPPORTED, "%s: head_dim=%d > 1024", fn, head_dim);
+  if (!dtype_ok(in_dtype)) return pa::fail(PA_EINVAL, "%s: bad in_dtype %d", fn, (int)in_dtype);
+  pa_status st = check_fp8_scales(fn, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  return pa::launch_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                    num_kv_heads, head_dim, block_size, num_blocks,
+                                    in_dtype == PA_BF16, k_scale, v_scale, stream);
+}
+
 extern "C" pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *block_pairs,
                                     int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int32_t num_blocks, pa_dtype kv_dtype,
@@ -71,7 +103,8 @@ extern "C" pa_status pa_copy_blocks(void *key_cache, void *value_cache, const in
   if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return pa::fail(PA_EINVAL, "%s: num_kv_heads=%d head_dim=%d block_size=%d num_blocks=%d", fn,
                     num_kv_heads, head_dim, block_size, num_blocks);
-  if (!dtype_ok(kv_dtype)) return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
+  if (!dtype_ok(kv_dtype) && kv_dtype != PA_FP8_E4M3)
+    return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
   if (num_pairs == 0) return PA_OK;
   if (!key_cache || !value_cache || !block_pairs)
     return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
@@ -115,6 +148,49 @@ extern "C" pa_status pa_decode(void *out, const void *query, const void *key_cac
   p.partition_size = 0;
   p.max_parts = 1;
   p.kv_bf16 = kv_dtype == PA_BF16;
+  p.out_bf16 = out_dtype == PA_BF16;
+  return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_decode_fp8(void *out, const void *query, const uint8_t *key_cache,
+                                   const uint8_t *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                   pa_dtype out_dtype, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_fp8";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale, PA_BF16);
+  if (st != PA_OK) return st;
+  st = check_fp8_scales(fn, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = 0;
+  p.max_parts = 1;
+  p.kv_bf16 = 0;
+  p.kv_fp8 = 1;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.out_bf16 = out_dtype == PA_BF16;
   return pa::launch_decode(p, stream);
 }
@@ -170,6 +246,54 @@ extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, flo
   p.partition_size = partition_size;
   p.max_parts = max_parts;
   p.kv_bf16 = kv_dtype == PA_BF16;
+  return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_decode_partitioned_fp8(
+    float *part_out, float *part_max, float *part_sum, const void *query,
+    const uint8_t *key_cache, const uint8_t *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_parts,
+    hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_partitioned_fp8";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale, PA_BF16);
+  if (st != PA_OK) return st;
+  st = check_fp8_scales(fn, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size % block_size != 0)
+    return pa::fail(PA_EINVAL, "%s: partition_size=%d must be >= 16 and a multiple of block_size=%d",
+                    fn, partition_size, block_size);
+  if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
+  if (num_seqs == 0) return PA_OK;
+  if (!part_out || !part_max || !part_sum || !query || !key_cache || !value_cache ||
+      !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = partition_size;
+  p.max_parts = max_parts;
+  p.kv_bf16 = 0;
+  p.kv_fp8 = 1;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   return pa::launch_decode(p, stream);
 }
 

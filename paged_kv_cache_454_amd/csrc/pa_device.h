@@ -54,6 +54,56 @@ struct Widen<bf16_t> {
   }
 };
 
+// E4M3FN code (one byte) of an FP8 cache.
+struct fp8_t {
+  uint8_t bits;
+};
+
+// Four E4M3FN codes (bytes of w, lowest first) as fp32 values. gfx950's
+// conversion implements the OCP E4M3FN format exactly (every code, NaN
+// codes included, decodes to its value; checked against the format's
+// definition).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *o) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo[0];
+  o[1] = lo[1];
+  o[2] = hi[0];
+  o[3] = hi[1];
+}
+
+// A lane's piece of one K or V row, widened to fp32: 16 bytes of fp32 or
+// BF16, or 8 bytes of E4M3 codes (so that the lane count per row matches a
+// BF16 query's). Q is the query's element type.
+template <typename KV>
+struct KvPiece;
+template <>
+struct KvPiece<float> {
+  static constexpr int N = 4;
+  using Q = float;
+  __device__ __forceinline__ static void load(const float *p, float *o) {
+    Widen<float>::apply(load16(p), o);
+  }
+};
+template <>
+struct KvPiece<bf16_t> {
+  static constexpr int N = 8;
+  using Q = bf16_t;
+  __device__ __forceinline__ static void load(const bf16_t *p, float *o) {
+    Widen<bf16_t>::apply(load16(p), o);
+  }
+};
+template <>
+struct KvPiece<fp8_t> {
+  static constexpr int N = 8;
+  using Q = bf16_t;
+  __device__ __forceinline__ static void load(const fp8_t *p, float *o) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    e4m3x4_to_f32(x.x, o);
+    e4m3x4_to_f32(x.y, o + 4);
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Store one output element as fp32 or bf16.

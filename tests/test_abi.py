@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_reduce",
               "pa_prefill_chunk", "pa_alloc_create", "pa_alloc_append", "pa_alloc_free",
-              "pa_alloc_block_table", "pa_last_error"]:
+              "pa_alloc_block_table", "pa_last_error", "pa_reshape_and_cache_fp8",
+              "pa_decode_fp8", "pa_decode_partitioned_fp8"]:
         assert n in names
 
 
@@ -107,6 +108,42 @@ def test_prefill_rejects_bad_arguments():
     st = lib.pa_prefill_chunk(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 16, 8192, 512, 24, 4,
                               256, 16, 400, 4000, 0.0625, 1, 0, NULL)
     assert st == _lib.PA_EINVAL
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    lib = _lib.lib()
+    w = lambda n, d, dt, ks, vs: lib.pa_reshape_and_cache_fp8(NULL, NULL, NULL, NULL, NULL, n, 4,
+                                                              d, 16, 10, dt, ks, vs, NULL)
+    assert w(5, 256, 1, 0.0, 1.0) == _lib.PA_EINVAL                # zero scale
+    assert w(5, 256, 1, 1.0, float("inf")) == _lib.PA_EINVAL
+    assert w(5, 256, 1, -2.0, 1.0) == _lib.PA_EINVAL
+    assert w(5, 256, _lib.PA_FP8_E4M3, 1.0, 1.0) == _lib.PA_EINVAL  # inputs are f32/bf16
+    assert w(5, 2048, 1, 1.0, 1.0) == _lib.PA_EUNSUPPORTED
+    assert w(5, 256, 1, 1.0, 1.0) == _lib.PA_EINVAL                # null pointers
+    assert w(0, 256, 1, 1.0, 1.0) == _lib.PA_OK                    # no tokens: no-op
+
+    def dec(hq=24, d=256, ks=1.0, vs=1.0, n=2, od=0):
+        return lib.pa_decode_fp8(NULL, NULL, NULL, NULL, NULL, NULL, n, hq, 4, d, 16, 8, 100,
+                                 0.0625, ks, vs, od, NULL)
+    assert dec(ks=float("nan")) == _lib.PA_EINVAL
+    assert dec(vs=0.0) == _lib.PA_EINVAL
+    assert dec(d=96) == _lib.PA_EUNSUPPORTED
+    assert dec(hq=25) == _lib.PA_EINVAL
+    assert dec(od=_lib.PA_FP8_E4M3) == _lib.PA_EINVAL
+    assert dec() == _lib.PA_EINVAL                                  # null pointers
+    assert dec(n=0) == _lib.PA_OK
+
+    def part(P=512, maxp=4, ks=1.0):
+        return lib.pa_decode_partitioned_fp8(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 2, 24,
+                                             4, 256, 16, 8, 100, 0.0625, ks, 1.0, P, maxp, NULL)
+    assert part(P=24) == _lib.PA_EINVAL
+    assert part(maxp=0) == _lib.PA_EINVAL
+    assert part(ks=-1.0) == _lib.PA_EINVAL
+    assert part() == _lib.PA_EINVAL                                 # null pointers
+    # FP8 pools are accepted by the block copy (no pairs: nothing launched)
+    assert lib.pa_copy_blocks(NULL, NULL, NULL, 0, 4, 256, 16, 10, _lib.PA_FP8_E4M3,
+                              NULL) == _lib.PA_OK
+    assert lib.pa_copy_blocks(NULL, NULL, NULL, 0, 4, 256, 16, 10, 3, NULL) == _lib.PA_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
