@@ -16,6 +16,11 @@ Inference", KV-cache section). The format is therefore a stated choice:
   fp32(scale)), the quotient rounded to fp32 as the kernel computes it
   (the quotient decides an integer code, so both sides form it in the same
   precision); the cache then holds decode(code) * scale.
+* Pool layouts: the key pool is [num_blocks][H_KV][block_size][d] like the
+  BF16 pools; the value pool stores each block transposed,
+  [num_blocks][H_KV][d][block_size] (the token index fastest), so that the
+  tokens of one channel are adjacent. The block table and the slot of a
+  token (block * block_size + offset) mean the same for both.
 """
 
 import numpy as np
@@ -80,25 +85,37 @@ def dequantize(codes, scale):
     return decode_e4m3(codes) * float(np.float32(scale))
 
 
+def value_rows(value_codes):
+    """A value code pool in the key pools' row layout [nb][H][bs][d]."""
+    return np.ascontiguousarray(np.swapaxes(value_codes, 2, 3))
+
+
+def value_pool(rows):
+    """Inverse of value_rows: [nb][H][bs][d] rows to the value pool layout."""
+    return np.ascontiguousarray(np.swapaxes(rows, 2, 3))
+
+
 def cache_write(key_codes, value_codes, key, value, slot_mapping, block_size, k_scale, v_scale):
     """The slot-mapped write of attention.cache_write, storing the codes of
-    key / k_scale and value / v_scale in copies of the two code pools."""
-    return attention.cache_write(key_codes, value_codes, quantize(key, k_scale),
-                                 quantize(value, v_scale), slot_mapping, block_size)
+    key / k_scale and value / v_scale in copies of the two code pools (the
+    value pool in its transposed block layout)."""
+    kc, vr = attention.cache_write(key_codes, value_rows(value_codes), quantize(key, k_scale),
+                                   quantize(value, v_scale), slot_mapping, block_size)
+    return kc, value_pool(vr)
 
 
 def decode(query, key_codes, value_codes, block_tables, context_lens, block_size, scale, k_scale,
            v_scale):
     """Decode attention over the dequantised cache (attention.decode)."""
     return attention.decode(query, dequantize(key_codes, k_scale),
-                            dequantize(value_codes, v_scale), block_tables, context_lens,
-                            block_size, scale)
+                            dequantize(value_rows(value_codes), v_scale), block_tables,
+                            context_lens, block_size, scale)
 
 
 def decode_partitions(query, key_codes, value_codes, block_tables, context_lens, block_size,
                       scale, k_scale, v_scale, partition_size, seqs=None, heads=None):
     """attention.decode_partitions over the dequantised cache."""
     return attention.decode_partitions(query, dequantize(key_codes, k_scale),
-                                       dequantize(value_codes, v_scale), block_tables,
+                                       dequantize(value_rows(value_codes), v_scale), block_tables,
                                        context_lens, block_size, scale, partition_size,
                                        seqs=seqs, heads=heads)

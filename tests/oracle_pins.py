@@ -561,7 +561,7 @@ def pin_fp8_cache(fp8):
     rng = np.random.default_rng(29)
     nb, hkv, bs, d = 6, 2, 4, 8
     kc = np.zeros((nb, hkv, bs, d), np.uint8)
-    vc = np.zeros((nb, hkv, bs, d), np.uint8)
+    vc = np.zeros((nb, hkv, d, bs), np.uint8)       # value blocks: token index fastest
     key = rng.standard_normal((5, hkv, d)).astype(np.float32)
     val = rng.standard_normal((5, hkv, d)).astype(np.float32)
     slots = np.array([3, 9, -1, 22, 0])
@@ -573,22 +573,24 @@ def pin_fp8_cache(fp8):
         qk = (torch.from_numpy(key[i]) / torch.tensor(ks, dtype=torch.float32))
         qv = (torch.from_numpy(val[i]) / torch.tensor(vs, dtype=torch.float32))
         assert np.array_equal(k2[sl // bs, :, sl % bs], qk.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
-        assert np.array_equal(v2[sl // bs, :, sl % bs], qv.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        assert np.array_equal(v2[sl // bs, :, :, sl % bs], qv.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
     assert int((k2 != 0).sum()) <= 4 * hkv * d and np.array_equal(k2[1], kc[1])  # block 1 unwritten
+    assert int((v2 != 0).sum()) <= 4 * hkv * d and np.array_equal(v2[1], vc[1])
     # values on the E4M3 grid times the scale survive exactly: fp8 decode = plain decode
     codes_k = rng.integers(0, 0x7E, size=(nb, hkv, bs, d)).astype(np.uint8)
-    codes_v = rng.integers(0, 0x7E, size=(nb, hkv, bs, d)).astype(np.uint8)
+    codes_v = rng.integers(0, 0x7E, size=(nb, hkv, d, bs)).astype(np.uint8)
     q = rng.standard_normal((2, 4, d))
     tables = np.array([[0, 3, -1], [5, 1, 2]])
     lens = np.array([7, 12])
     got = fp8.decode(q, codes_k, codes_v, tables, lens, bs, 0.3, 0.25, 2.0)
     want = attention_decode_ref(q, fp8.decode_e4m3(codes_k) * 0.25, fp8.decode_e4m3(codes_v) * 2.0,
-                                tables, lens, bs, 0.3)
+                                tables, lens, bs, 0.3, v_tokens_last=True)
     assert np.abs(got - want).max() < 1e-12
 
 
-def attention_decode_ref(q, kc, vc, tables, lens, bs, scale):
-    """Brute-force decode (loops), for the fp8 pin."""
+def attention_decode_ref(q, kc, vc, tables, lens, bs, scale, v_tokens_last=False):
+    """Brute-force decode (loops), for the fp8 pin; v_tokens_last: the value
+    pool is [nb][H][d][bs]."""
     out = np.zeros(q.shape)
     hq, hkv = q.shape[1], kc.shape[1]
     for s in range(q.shape[0]):
@@ -603,7 +605,7 @@ def attention_decode_ref(q, kc, vc, tables, lens, bs, scale):
             acc = np.zeros(q.shape[2])
             for t, wt in enumerate(w):
                 blk = int(tables[s][t // bs])
-                acc += wt * vc[blk, g, t % bs]
+                acc += wt * (vc[blk, g, :, t % bs] if v_tokens_last else vc[blk, g, t % bs])
             out[s, h] = acc / sum(w)
     return out
 

@@ -78,6 +78,9 @@ MUTATIONS += [
     ("fp8", "    return decode_e4m3(codes) * float(np.float32(scale))",
      "    return decode_e4m3(codes)"),
     ("fp8", "        s = 0x80 if np.signbit(x) else 0", "        s = 0x80 if x < 0 else 0"),
+    ("fp8", "    return np.ascontiguousarray(np.swapaxes(value_codes, 2, 3))",
+     "    return np.ascontiguousarray(value_codes)"),
+    ("fp8", "    return kc, value_pool(vr)", "    return kc, vr"),
 ]
 
 PINS = {"attention": P.ATTENTION_PINS, "accounting": P.ACCOUNTING_PINS,
