@@ -340,7 +340,9 @@ def fp8_leg(layers, meta, P, steps, warmup, dev):
     def codes(x, sc):
         return (x.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
 
-    pools = [(codes(L["key_cache"], ks), codes(L["value_cache"], vs)) for L in layers]
+    # value pools store each block transposed ([H][d][bs] per block)
+    pools = [(codes(L["key_cache"], ks), codes(L["value_cache"].transpose(2, 3), vs).contiguous())
+             for L in layers]
     torch.cuda.synchronize()
     lens = meta["lens"]
     S = len(lens)

@@ -57,6 +57,20 @@ def _pool_shape(key_cache, value_cache):
     return key_cache.shape
 
 
+def _fp8_pool_shape(key_cache, value_cache):
+    """FP8 pools: keys [num_blocks][H_KV][block_size][d], values with each
+    block transposed, [num_blocks][H_KV][d][block_size]; uint8 codes (or
+    float8_e4m3fn)."""
+    if key_cache.dtype not in _FP8 or value_cache.dtype not in _FP8:
+        raise ValueError("FP8 pools must be uint8 or float8_e4m3fn")
+    if key_cache.dim() != 4 or value_cache.dim() != 4:
+        raise ValueError("pools are 4-d: keys [nb][H][bs][d], values [nb][H][d][bs]")
+    nb, hkv, bs, d = key_cache.shape
+    if tuple(value_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError("the FP8 value pool must be [num_blocks][num_kv_heads][head_dim][block_size]")
+    return key_cache.shape
+
+
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
     """Write key/value [num_tokens][H_KV][d] into the pools at slot_mapping."""
     num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
@@ -76,11 +90,12 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
 def pa_copy_blocks(key_cache, value_cache, block_pairs, stream=None):
     """Copy whole blocks inside both pools: block_pairs is int32 [n][2] of
     (source, destination) ids (the allocator's copy-on-write pairs)."""
-    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    fp8 = key_cache.dtype in _FP8
+    num_blocks, hkv, bs, d = (_fp8_pool_shape if fp8 else _pool_shape)(key_cache, value_cache)
     if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be int32 [num_pairs][2]")
     n = block_pairs.shape[0]
-    dt = PA_FP8_E4M3 if key_cache.dtype in _FP8 else _dtype(key_cache, "pools")
+    dt = PA_FP8_E4M3 if fp8 else _dtype(key_cache, "pools")
     check(lib().pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
                                _dev(block_pairs, "block_pairs", torch.int32), n, hkv, d, bs,
                                num_blocks, dt, _stream(stream)))
@@ -91,9 +106,7 @@ def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k
     """Quantising write: the E4M3 codes of key / k_scale and value / v_scale
     (key/value float32 or bfloat16 [num_tokens][H_KV][d]) go into the uint8
     (or float8_e4m3fn) pools at slot_mapping."""
-    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
-    if key_cache.dtype not in _FP8:
-        raise ValueError("pools must be uint8 or float8_e4m3fn")
+    num_blocks, hkv, bs, d = _fp8_pool_shape(key_cache, value_cache)
     if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
         raise ValueError("key/value must be [num_tokens][num_kv_heads][head_dim] matching the pools")
     if key.dtype != value.dtype:
@@ -109,7 +122,7 @@ def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k
 
 def _attn_common(query, key_cache, value_cache, block_tables, context_lens, rows_name,
                  fp8=False):
-    num_blocks, hkv, bs, d = _pool_shape(key_cache, value_cache)
+    num_blocks, hkv, bs, d = (_fp8_pool_shape if fp8 else _pool_shape)(key_cache, value_cache)
     if query.dim() != 3 or query.shape[2] != d:
         raise ValueError(f"query must be [{rows_name}][num_q_heads][{d}]")
     if fp8:

@@ -144,6 +144,14 @@ __device__ __forceinline__ void load_vals<float, 1>(const float *p, float *o) {
 
 template <int VEC>
 __device__ __forceinline__ void store_codes(uint8_t *dst, const float *x, float scale);
+// Value pools store each block transposed: consecutive channels are
+// block_size bytes apart.
+template <int VEC>
+__device__ __forceinline__ void store_codes_strided(uint8_t *dst, const float *x, float scale,
+                                                    int stride) {
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) dst[(int64_t)v * stride] = (uint8_t)f32_to_e4m3(x[v] / scale);
+}
 template <>
 __device__ __forceinline__ void store_codes<8>(uint8_t *dst, const float *x, float scale) {
   uint32_t w[2];
@@ -184,8 +192,9 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
     const int64_t blk = slot / block_size;
     const int64_t off = slot - blk * block_size;
     const int64_t dst = ((blk * num_kv_heads + head) * block_size + off) * head_dim + piece * VEC;
+    const int64_t vdst = ((blk * num_kv_heads + head) * head_dim + piece * VEC) * block_size + off;
     store_codes<VEC>(key_cache + dst, kx, k_scale);
-    store_codes<VEC>(value_cache + dst, vx, v_scale);
+    store_codes_strided<VEC>(value_cache + vdst, vx, v_scale, block_size);
   }
 }
 

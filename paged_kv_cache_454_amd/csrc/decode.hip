@@ -143,12 +143,15 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
   const int64_t head_stride = (int64_t)bs * HEAD_DIM;
   const int64_t block_stride = head_stride * p.num_kv_heads;
   const KV *kbase = reinterpret_cast<const KV *>(p.key_cache) + kvh * head_stride + c * VEC;
-  const KV *vbase = reinterpret_cast<const KV *>(p.value_cache) + kvh * head_stride + c * VEC;
+  // An FP8 value pool stores each block transposed ([head_dim][block_size]):
+  // channel ch of token offset o sits at ch * bs + o.
+  const KV *vbase = reinterpret_cast<const KV *>(p.value_cache) + kvh * head_stride +
+                    (F8 ? (int64_t)c * VEC * bs : (int64_t)c * VEC);
 
   for (int t0 = lo + wave * RPL; t0 < hi; t0 += NW * RPL) {
     const int t = t0 + r;
     bool valid = t < hi;
-    int64_t off = 0;
+    int64_t off = 0, voff = 0;
     if (valid) {
       const int blk = table[t / bs];
       if (blk < 0 || blk >= p.num_blocks) {
@@ -156,12 +159,22 @@ __global__ __launch_bounds__(NW * 64) void decode_generic_kernel(DecodeParams p)
         valid = false;
       } else {
         off = (int64_t)blk * block_stride + (int64_t)(t % bs) * HEAD_DIM;
+        voff = F8 ? (int64_t)blk * block_stride + t % bs : off;
       }
     }
     float kf[VEC], vf[VEC];
     if (valid) {
       Piece::load(kbase + off, kf);
-      Piece::load(vbase + off, vf);
+      if constexpr (F8) {
+        const uint8_t *vp = reinterpret_cast<const uint8_t *>(vbase + voff);
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) w[v / 4] |= (uint32_t)vp[(int64_t)v * bs] << (8 * (v % 4));
+        e4m3x4_to_f32(w[0], vf);
+        e4m3x4_to_f32(w[1], vf + 4);
+      } else {
+        Piece::load(vbase + voff, vf);
+      }
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) kf[v] = vf[v] = 0.f;
@@ -284,6 +297,7 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = rows * p.num_kv_heads * parts;
   if (grid == 0) return PA_OK;
   if (grid > 0x7fffffff) return fail(PA_EUNSUPPORTED, "decode: grid of %lld workgroups", (long long)grid);
+  if (launch_decode_fp8(p, stream)) return check_launch("decode");
   if (launch_decode_persistent(p, stream)) return check_launch("decode");
   if (launch_decode_tiled(p, (unsigned)grid, stream)) return check_launch("decode");
   if (p.kv_fp8)

@@ -46,52 +46,21 @@
 
 #include "launch.h"
 #include "pa_device.h"
+#include "persistent_plan.h"
 
 namespace pa {
 namespace {
+using namespace persist;
 
 constexpr int D = 256;       // head_dim
 constexpr int TILE = 16;     // tokens per tile
 constexpr int LOADS = 8;     // 1 KiB wavefront loads per 8 KiB K (or V) tile
 constexpr int RSTRIDE = 20;  // floats per LDS reduction row (16 + pad)
 constexpr int NW = 8;        // wavefronts per workgroup (two per SIMD)
-constexpr int MAXU = 64;     // candidate units per workgroup (one per lane)
 constexpr float kLazy = 8.f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// One lane's share of a 1 KiB (BF16) or 512-byte (E4M3) wavefront load: the
-// 8 channels 8*(l%32).. of one token, as 16 or 8 bytes.
-template <bool KV8>
-struct RingElem {
-  using T = vec16;
-};
-template <>
-struct RingElem<true> {
-  using T = u32x2;
-};
-
-// BF16 pair W (channels 2W, 2W+1) of a lane's 8 channels. E4M3 codes widen
-// to BF16 exactly (3 of BF16's 7 mantissa bits, exponents 2^-9..2^8), two
-// per v_cvt_scalef32_pk_bf16_fp8 with scale 1.
-template <int W>
-__device__ __forceinline__ uint32_t bf16_pair(const vec16 &v) {
-  return v.w[W];
-}
-template <int W>
-__device__ __forceinline__ uint32_t bf16_pair(const u32x2 &v) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[W >> 1], 1.0f, (W & 1) != 0));
-}
-template <typename R>
-__device__ __forceinline__ void bf16_pairs(const R &v, uint32_t (&o)[4]) {
-  o[0] = bf16_pair<0>(v);
-  o[1] = bf16_pair<1>(v);
-  o[2] = bf16_pair<2>(v);
-  o[3] = bf16_pair<3>(v);
-}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -154,200 +123,10 @@ struct Desc {
   int nvalid;   // valid tokens of the tile (0: empty, loads return zeros)
 };
 
-// Partitions of one sequence: T (context clamped to the table's capacity),
-// full partitions, whether a last, partial one follows, and whether the
-// sequence's outputs must be poisoned (context longer than the table or, in
-// split mode, than max_parts partitions).
-struct SeqParts {
-  int T, nfull, partial, bad;
-};
-
-// 32-bit arithmetic throughout: the host guarantees max_blocks_per_seq *
-// block_size < 2^31, so the clamped T fits.
-template <bool SPLIT>
-__device__ __forceinline__ SeqParts seq_parts(const DecodeParams &p, int s) {
-  SeqParts r{0, 0, 0, 0};
-  if (s >= p.num_seqs) return r;
-  int T = p.context_lens[s];
-  T = T < 0 ? 0 : T;
-  const int cap = p.max_blocks_per_seq * p.block_size;
-  if (T > cap) {
-    r.bad = 1;
-    T = cap;
-  }
-  r.T = T;
-  if (SPLIT) {
-    const unsigned P = (unsigned)p.partition_size;
-    unsigned nf = (unsigned)T / P;
-    unsigned np = nf + ((unsigned)T != nf * P);  // ceil(T / P)
-    if (np > (unsigned)p.max_parts) {
-      r.bad = 1;  // T > max_parts * P
-      np = (unsigned)p.max_parts;
-    }
-    if (nf > np) nf = np;
-    r.nfull = (int)nf;
-    r.partial = np > nf;
-  } else {
-    r.partial = 1;  // one unit per sequence (an empty one still writes zeros)
-  }
-  return r;
-}
-
-// The planner's lanes exchange values through LDS. A wavefront's LDS
-// operations execute in program order, but the compiler treats each lane as
-// a thread of its own and may move one lane's store past loads that only the
-// other lanes make (it has merged such a store into a later one). This
-// compiler barrier keeps every memory operation on its side.
-__device__ __forceinline__ void lane_exchange_fence() { asm volatile("" ::: "memory"); }
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(x, d, 64);
-    if (lane >= d) x += t;
-  }
-  return x;
-}
-
-// First index i in [0, 64) with incl[i] > off (incl non-decreasing).
-__device__ __forceinline__ int upper_index(const int *incl, int off) {
-  int lo = 0, hi = 63;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (incl[mid] > off)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return lo;
-}
-
-// The workgroup's units, one per lane: lane k holds the unit assigned in
-// round k. Units are enumerated as all full partitions (sequence-major)
-// followed by the last, partial partitions ordered by decreasing size (for
-// up to 64 sequences; in sequence order beyond that), and dealt to the
-// workgroups in snake order (round k goes 0..grid-1 when k is even,
-// grid-1..0 when odd). Big units go first and the round-by-round reversal
-// evens out the loads; in single-pass mode every sequence is one partial
-// unit, so the longest contexts start first. Run by one wavefront.
-// scr: 192 ints of this wave's LDS (prologue scratch).
-template <bool SPLIT>
-__device__ void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit, int &bad_part,
-                           int &active) {
-  const int S = p.num_seqs, H = p.num_kv_heads;
-  const int NB = gridDim.x, b = blockIdx.x;
-  const int a = lane * NB + ((lane & 1) ? NB - 1 - b : b);
-  const int P = SPLIT ? p.partition_size : 0;
-  int c_s = -1, c_h = 0, c_p = 0, c_T = 0, c_bad = 0;
-
-  // Full partitions, sequence-major. The first 64 sequences' counts are
-  // loaded once and serve the partial partitions below as well.
-  const SeqParts sp_first = seq_parts<SPLIT>(p, lane);
-  int F = 0;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const SeqParts sp = s0 == 0 ? sp_first : seq_parts<SPLIT>(p, s0 + lane);
-    const int incl = wave_incl_scan(sp.nfull * H, lane);
-    const int tot = __shfl(incl, 63, 64);
-    lane_exchange_fence();
-    scr[lane] = incl;
-    lane_exchange_fence();
-    const int off = a - F;
-    const bool hit = off >= 0 && off < tot;
-    const int i = hit ? upper_index(scr, off) : lane;
-    const int T_i = __shfl(sp.T, i, 64), bad_i = __shfl(sp.bad, i, 64);
-    if (hit) {
-      const int r = off - (i ? scr[i - 1] : 0);
-      c_s = s0 + i;
-      c_p = r / H;
-      c_h = r - c_p * H;
-      c_T = T_i;
-      c_bad = bad_i;
-    }
-    F += tot;
-  }
-
-  // Last, partial partitions.
-  int NPH = 0;  // partial units
-  if (S <= 64) {
-    const SeqParts sp = sp_first;
-    // A unique key per sequence that orders by decreasing size, then by
-    // increasing sequence index; the rank is the count of larger keys.
-    // Every lane reads all 64 keys from LDS (broadcast reads, no serial
-    // dependency); lanes past S hold -1.
-    const int sz = sp.T - sp.nfull * P;
-    const int key = sp.partial ? (min(sz, (1 << 25) - 1) << 6) | (63 - lane) : -1;
-    scr[128 + lane] = key;
-    lane_exchange_fence();
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < 64; j += 4) {
-      const int4 k4 = *reinterpret_cast<const int4 *>(&scr[128 + j]);
-      rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
-    }
-    lane_exchange_fence();
-    if (sp.partial) scr[64 + rank] = lane;
-    lane_exchange_fence();
-    const int nps = __popcll(__builtin_amdgcn_ballot_w64(sp.partial != 0));
-    NPH = nps * H;
-    const int off = a - F;
-    const bool hit = off >= 0 && off < NPH;
-    const int q = hit ? off / H : 0;
-    const int sel = hit ? scr[64 + q] : lane;
-    const int T_i = __shfl(sp.T, sel, 64), bad_i = __shfl(sp.bad, sel, 64);
-    const int nf_i = __shfl(sp.nfull, sel, 64);
-    if (hit) {
-      c_s = sel;
-      c_h = off - q * H;
-      c_p = nf_i;
-      c_T = T_i;
-      c_bad = bad_i;
-    }
-  } else {
-    for (int s0 = 0; s0 < S; s0 += 64) {
-      const SeqParts sp = seq_parts<SPLIT>(p, s0 + lane);
-      const int incl = wave_incl_scan(sp.partial * H, lane);
-      const int tot = __shfl(incl, 63, 64);
-      lane_exchange_fence();
-      scr[lane] = incl;
-      lane_exchange_fence();
-      const int off = a - F - NPH;
-      const bool hit = off >= 0 && off < tot;
-      const int i = hit ? upper_index(scr, off) : lane;
-      const int T_i = __shfl(sp.T, i, 64), bad_i = __shfl(sp.bad, i, 64);
-      const int nf_i = __shfl(sp.nfull, i, 64);
-      if (hit) {
-        c_s = s0 + i;
-        c_h = off - (i ? scr[i - 1] : 0);
-        c_p = nf_i;
-        c_T = T_i;
-        c_bad = bad_i;
-      }
-      NPH += tot;
-    }
-  }
-
-  // Only a unit inside the batch is ever entered.
-  active = c_s >= 0 && c_s < S && c_h >= 0 && c_h < H && c_T >= 0;
-  if (!active) {
-    unit = make_int4(0, 0, 0, 0);
-    bad_part = 0;
-    return;
-  }
-  int lo = 0, hi = c_T;
-  if (SPLIT) {
-    lo = c_p * P;
-    hi = c_T < lo + P ? c_T : lo + P;
-  }
-  unit = make_int4(c_s, c_h, lo, hi);
-  bad_part = c_p * 2 + c_bad;
-}
-
-template <int G, bool SPLIT, bool KV8>
+template <int G, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_persistent_kernel(DecodeParams p) {
   using C = Cfg<G>;
-  using RE = typename RingElem<KV8>::T;
-  constexpr int EB = KV8 ? 1 : 2;  // bytes per cached element
   __shared__ __attribute__((aligned(16))) float red_all[NW][C::RED];
   __shared__ __attribute__((aligned(16))) uint32_t pl_all[NW][2][4][8];  // [parity][pair][head]
   __shared__ float alpha_all[NW][8];
@@ -391,8 +170,8 @@ void decode_persistent_kernel(DecodeParams p) {
   const int bs = p.block_size;
   const int64_t head_stride = (int64_t)bs * D;
   const int64_t block_stride = head_stride * H;
-  const uint8_t *kpool = reinterpret_cast<const uint8_t *>(p.key_cache);
-  const uint8_t *vpool = reinterpret_cast<const uint8_t *>(p.value_cache);
+  const uint16_t *kpool = reinterpret_cast<const uint16_t *>(p.key_cache);
+  const uint16_t *vpool = reinterpret_cast<const uint16_t *>(p.value_cache);
   // The whole block table as one buffer (the host checks it fits 2^31 bytes).
   const __amdgpu_buffer_rsrc_t tab_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(p.block_tables), (short)0,
@@ -466,7 +245,7 @@ void decode_persistent_kernel(DecodeParams p) {
   struct TileRsrc {
     __amdgpu_buffer_rsrc_t lo, hi;
   };
-  auto tile_rsrc = [&](const Desc &d, const uint8_t *pool, int &nvalid, int &bad) {
+  auto tile_rsrc = [&](const Desc &d, const uint16_t *pool, int &nvalid, int &bad) {
     int blk = __builtin_amdgcn_readfirstlane(d.blk), n = d.nvalid;
     bad = 0;
     if (n > 0 && (blk < 0 || blk >= p.num_blocks)) {
@@ -475,34 +254,28 @@ void decode_persistent_kernel(DecodeParams p) {
     }
     if (n <= 0) blk = 0;
     nvalid = n;
-    const uint8_t *base =
-        pool + ((int64_t)blk * block_stride + (int64_t)d.head * head_stride + (int64_t)d.tok_off * D) *
-                   EB;
+    const uint16_t *base =
+        pool + (int64_t)blk * block_stride + (int64_t)d.head * head_stride + (int64_t)d.tok_off * D;
     const int n_lo = n < 8 ? n : 8, n_hi = n > 8 ? n - 8 : 0;
     TileRsrc r;
-    r.lo = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0,
-                                             n_lo * D * EB, 0x00020000);
-    r.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base + 8 * D * EB), (short)0,
-                                             n_hi * D * EB, 0x00020000);
+    r.lo = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0,
+                                             n_lo * D * 2, 0x00020000);
+    r.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + 8 * D), (short)0,
+                                             n_hi * D * 2, 0x00020000);
     return r;
   };
-  const int lane_off = lane * 8 * EB;
-  auto load8 = [&](RE(&kt)[LOADS], const TileRsrc &r) {
+  const int lane_off = lane * 16;
+  auto load8 = [&](vec16(&kt)[LOADS], const TileRsrc &r) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       // Vector offset + immediate offset: both are range-checked against
       // num_records (the scalar offset would not be).
-      if constexpr (KV8) {
-        kt[i] = __builtin_amdgcn_raw_buffer_load_b64(i < 4 ? r.lo : r.hi,
-                                                     lane_off + (i & 3) * 512, 0, kStreamLoad);
-      } else {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-            i < 4 ? r.lo : r.hi, lane_off + (i & 3) * 1024, 0, kStreamLoad);
-        kt[i].w[0] = x[0];
-        kt[i].w[1] = x[1];
-        kt[i].w[2] = x[2];
-        kt[i].w[3] = x[3];
-      }
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+          i < 4 ? r.lo : r.hi, lane_off + (i & 3) * 1024, 0, kStreamLoad);
+      kt[i].w[0] = x[0];
+      kt[i].w[1] = x[1];
+      kt[i].w[2] = x[2];
+      kt[i].w[3] = x[3];
     }
   };
 
@@ -510,7 +283,7 @@ void decode_persistent_kernel(DecodeParams p) {
   // of the next two, in the same order as the loop body issues them (tile,
   // id two ahead, tile, id two ahead), so the compiler's wait counts inside
   // the loop are the steady-state ones from the first iteration on.
-  RE ka[LOADS], va[LOADS], kb[LOADS], vb[LOADS];
+  vec16 ka[LOADS], va[LOADS], kb[LOADS], vb[LOADS];
   int nv_a, nv_b, bad_a, bad_b;
   Desc dn, dn2;  // descriptors of the tiles two and three positions ahead
   {
@@ -546,32 +319,26 @@ void decode_persistent_kernel(DecodeParams p) {
   stage_queries(act_mask);
   __syncthreads();
 
-  // An FP8 cache holds K / k_scale and V / v_scale: the K scale folds into
-  // the logit scale, the V scale into the unit's outputs.
-  const float sl2 = p.scale * kLog2e * (KV8 ? p.k_scale : 1.f);
-  const float vsc = KV8 ? p.v_scale : 1.f;
+  const float sl2 = p.scale * kLog2e;
   float acc[G][8];
   float m_r[C::ROUNDS], l_r[C::ROUNDS];
 
   // Q.K for one tile: partial dot products over this lane's 8 channels,
   // summed over lanes c and c+16 of each token with one swap + add for two
   // values at a time, then parked in LDS for the transposed read-back.
-  auto qk = [&](const RE(&kt)[LOADS], int qslot) {
-    uint32_t kw[LOADS][4];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) bf16_pairs(kt[i], kw[i]);
+  auto qk = [&](const vec16(&kt)[LOADS], int qslot) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4 qv = qs[qslot][h][lane & 31];
       const uint32_t qh[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float s0 = dot2(qh[0], kw[2 * j][0], 0.f);
-        float s1 = dot2(qh[0], kw[2 * j + 1][0], 0.f);
+        float s0 = dot2(qh[0], kt[2 * j].w[0], 0.f);
+        float s1 = dot2(qh[0], kt[2 * j + 1].w[0], 0.f);
 #pragma unroll
         for (int w = 1; w < 4; ++w) {
-          s0 = dot2(qh[w], kw[2 * j][w], s0);
-          s1 = dot2(qh[w], kw[2 * j + 1][w], s1);
+          s0 = dot2(qh[w], kt[2 * j].w[w], s0);
+          s1 = dot2(qh[w], kt[2 * j + 1].w[w], s1);
         }
         const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s1),
                                                         false, false);
@@ -582,7 +349,7 @@ void decode_persistent_kernel(DecodeParams p) {
   };
 
   // Softmax and P.V for one tile whose partial logits are in LDS.
-  auto softmax_pv = [&](int nvalid, const RE(&vt)[LOADS]) {
+  auto softmax_pv = [&](int nvalid, const vec16(&vt)[LOADS]) {
     float z[C::ROUNDS];
 #pragma unroll
     for (int rd = 0; rd < C::ROUNDS; ++rd) {
@@ -637,9 +404,6 @@ void decode_persistent_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t vwa[4], vwb[4];
-      bf16_pairs(vt[2 * j], vwa);
-      bf16_pairs(vt[2 * j + 1], vwb);
       uint32_t pp[8];
       const uint4 p0 = *reinterpret_cast<const uint4 *>(&pl[tau][j][0]);
       const uint4 p1 = *reinterpret_cast<const uint4 *>(&pl[tau][j][4]);
@@ -647,7 +411,7 @@ void decode_persistent_kernel(DecodeParams p) {
       pp[4] = p1.x; pp[5] = p1.y; pp[6] = p1.z; pp[7] = p1.w;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t va_ = vwa[w], vb_ = vwb[w];
+        const uint32_t va_ = vt[2 * j].w[w], vb_ = vt[2 * j + 1].w[w];
         const uint32_t lo2 = __builtin_amdgcn_perm(vb_, va_, 0x05040100u);
         const uint32_t hi2 = __builtin_amdgcn_perm(vb_, va_, 0x07060302u);
 #pragma unroll
@@ -764,7 +528,7 @@ void decode_persistent_kernel(DecodeParams p) {
       }
       constexpr int kDrop = 0x7ffffff0;
       if constexpr (!split) {
-        const float o = bad ? nan : (L > 0.f ? A / L * vsc : 0.f);
+        const float o = bad ? nan : (L > 0.f ? A / L : 0.f);
         const int64_t e = (qrow + h) * D + ch;
         if (p.out_bf16)
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(o), out_rsrc, live ? (int)(e * 2) : kDrop,
@@ -774,7 +538,7 @@ void decode_persistent_kernel(DecodeParams p) {
                                                 live ? (int)(e * 4) : kDrop, 0, 0);
       } else {
         const int64_t pidx = (qrow + h) * p.max_parts + part;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bad ? nan : A / L * vsc), out_rsrc,
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bad ? nan : A / L), out_rsrc,
                                               live ? (int)((pidx * D + ch) * 4) : kDrop, 0, 0);
         const int moff = (live && ch == 0) ? (int)(pidx * 4) : kDrop;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bad ? nan : M * kLn2), max_rsrc, moff,
@@ -786,29 +550,14 @@ void decode_persistent_kernel(DecodeParams p) {
   }
 }
 
-int num_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 }  // namespace
 
 // Launch the persistent kernel when the shape is one it covers; false
 // otherwise (the caller then uses the generic kernel).
 bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream) {
-  if ((!p.kv_bf16 && !p.kv_fp8) || p.head_dim != D || p.block_size % TILE != 0 ||
-      p.query_start_loc)
+  if (!p.kv_bf16 || p.head_dim != D || p.block_size % TILE != 0 || p.query_start_loc)
     return false;
-  const bool kv8 = p.kv_fp8 != 0;
   if (p.partition_size > 0 && p.partition_size % TILE != 0) return false;
   if ((int64_t)p.num_seqs * p.max_blocks_per_seq * 4 > 0x7fffffff) return false;
   const int group = p.num_q_heads / p.num_kv_heads;
@@ -821,9 +570,7 @@ bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream) {
   // for its planner and ring: with at most one unit per CU, or with
   // partitions under 2 tiles per wavefront, where padding every wavefront's
   // share of a unit to an even count would leave half the ring empty.
-  // (An FP8 cache has no tiled kernel and stays here.)
-  if (!kv8 && p.partition_size > 0 && (units <= grid || p.partition_size < 2 * NW * TILE))
-    return false;
+  if (p.partition_size > 0 && (units <= grid || p.partition_size < 2 * NW * TILE)) return false;
   if (grid > units) grid = units;
   if (grid * MAXU < units) return false;  // more than 64 units per workgroup
   const int64_t out_bytes = (int64_t)p.num_seqs * p.num_q_heads * parts * D *
@@ -831,16 +578,12 @@ bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream) {
   if (out_bytes > 0x7fff0000) return false;
   const bool split = p.partition_size > 0;
   switch (group) {
-#define PA_CASE(g)                                                                         \
-  case g:                                                                                  \
-    if (kv8 && split)                                                                      \
-      decode_persistent_kernel<g, true, true><<<(unsigned)grid, NW * 64, 0, stream>>>(p);  \
-    else if (kv8)                                                                          \
-      decode_persistent_kernel<g, false, true><<<(unsigned)grid, NW * 64, 0, stream>>>(p); \
-    else if (split)                                                                        \
-      decode_persistent_kernel<g, true, false><<<(unsigned)grid, NW * 64, 0, stream>>>(p); \
-    else                                                                                   \
-      decode_persistent_kernel<g, false, false><<<(unsigned)grid, NW * 64, 0, stream>>>(p); \
+#define PA_CASE(g)                                                                        \
+  case g:                                                                                 \
+    if (split)                                                                            \
+      decode_persistent_kernel<g, true><<<(unsigned)grid, NW * 64, 0, stream>>>(p); \
+    else                                                                                  \
+      decode_persistent_kernel<g, false><<<(unsigned)grid, NW * 64, 0, stream>>>(p); \
     return true;
     PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
 #undef PA_CASE

@@ -64,6 +64,11 @@ bool launch_decode_tiled(const DecodeParams &p, unsigned grid, hipStream_t strea
 // false when the shape is not covered.
 bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream);
 
+// Matrix-core decode over FP8 pools (head_dim 256, block_size % 16 == 0,
+// partitions of a multiple of 32 tokens). Returns false when the shape is
+// not covered.
+bool launch_decode_fp8(const DecodeParams &p, hipStream_t stream);
+
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

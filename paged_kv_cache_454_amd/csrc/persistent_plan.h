@@ -1,0 +1,220 @@
+// Unit planning shared by the persistent decode kernels (device code, not
+// installed). A unit is one (sequence, KV head, partition) - or one
+// (sequence, KV head) in single-pass mode - and produces one output record;
+// each persistent workgroup owns up to MAXU units, planned by one wavefront
+// at kernel start from the device-side context lengths.
+#pragma once
+
+#include "launch.h"
+#include "pa_device.h"
+
+namespace pa {
+namespace persist {
+
+constexpr int MAXU = 64;  // candidate units per workgroup (one per lane)
+
+// Partitions of one sequence: T (context clamped to the table's capacity),
+// full partitions, whether a last, partial one follows, and whether the
+// sequence's outputs must be poisoned (context longer than the table or, in
+// split mode, than max_parts partitions).
+struct SeqParts {
+  int T, nfull, partial, bad;
+};
+
+// 32-bit arithmetic throughout: the host guarantees max_blocks_per_seq *
+// block_size < 2^31, so the clamped T fits.
+template <bool SPLIT>
+__device__ __forceinline__ SeqParts seq_parts(const DecodeParams &p, int s) {
+  SeqParts r{0, 0, 0, 0};
+  if (s >= p.num_seqs) return r;
+  int T = p.context_lens[s];
+  T = T < 0 ? 0 : T;
+  const int cap = p.max_blocks_per_seq * p.block_size;
+  if (T > cap) {
+    r.bad = 1;
+    T = cap;
+  }
+  r.T = T;
+  if (SPLIT) {
+    const unsigned P = (unsigned)p.partition_size;
+    unsigned nf = (unsigned)T / P;
+    unsigned np = nf + ((unsigned)T != nf * P);  // ceil(T / P)
+    if (np > (unsigned)p.max_parts) {
+      r.bad = 1;  // T > max_parts * P
+      np = (unsigned)p.max_parts;
+    }
+    if (nf > np) nf = np;
+    r.nfull = (int)nf;
+    r.partial = np > nf;
+  } else {
+    r.partial = 1;  // one unit per sequence (an empty one still writes zeros)
+  }
+  return r;
+}
+
+// The planner's lanes exchange values through LDS. A wavefront's LDS
+// operations execute in program order, but the compiler treats each lane as
+// a thread of its own and may move one lane's store past loads that only the
+// other lanes make (it has merged such a store into a later one). This
+// compiler barrier keeps every memory operation on its side.
+__device__ __forceinline__ void lane_exchange_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d, 64);
+    if (lane >= d) x += t;
+  }
+  return x;
+}
+
+// First index i in [0, 64) with incl[i] > off (incl non-decreasing).
+__device__ __forceinline__ int upper_index(const int *incl, int off) {
+  int lo = 0, hi = 63;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (incl[mid] > off)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+// The workgroup's units, one per lane: lane k holds the unit assigned in
+// round k. Units are enumerated as all full partitions (sequence-major)
+// followed by the last, partial partitions ordered by decreasing size (for
+// up to 64 sequences; in sequence order beyond that), and dealt to the
+// workgroups in snake order (round k goes 0..grid-1 when k is even,
+// grid-1..0 when odd). Big units go first and the round-by-round reversal
+// evens out the loads; in single-pass mode every sequence is one partial
+// unit, so the longest contexts start first. Run by one wavefront.
+// scr: 192 ints of this wave's LDS (prologue scratch).
+template <bool SPLIT>
+__device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int4 &unit, int &bad_part,
+                           int &active) {
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  const int NB = gridDim.x, b = blockIdx.x;
+  const int a = lane * NB + ((lane & 1) ? NB - 1 - b : b);
+  const int P = SPLIT ? p.partition_size : 0;
+  int c_s = -1, c_h = 0, c_p = 0, c_T = 0, c_bad = 0;
+
+  // Full partitions, sequence-major. The first 64 sequences' counts are
+  // loaded once and serve the partial partitions below as well.
+  const SeqParts sp_first = seq_parts<SPLIT>(p, lane);
+  int F = 0;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const SeqParts sp = s0 == 0 ? sp_first : seq_parts<SPLIT>(p, s0 + lane);
+    const int incl = wave_incl_scan(sp.nfull * H, lane);
+    const int tot = __shfl(incl, 63, 64);
+    lane_exchange_fence();
+    scr[lane] = incl;
+    lane_exchange_fence();
+    const int off = a - F;
+    const bool hit = off >= 0 && off < tot;
+    const int i = hit ? upper_index(scr, off) : lane;
+    const int T_i = __shfl(sp.T, i, 64), bad_i = __shfl(sp.bad, i, 64);
+    if (hit) {
+      const int r = off - (i ? scr[i - 1] : 0);
+      c_s = s0 + i;
+      c_p = r / H;
+      c_h = r - c_p * H;
+      c_T = T_i;
+      c_bad = bad_i;
+    }
+    F += tot;
+  }
+
+  // Last, partial partitions.
+  int NPH = 0;  // partial units
+  if (S <= 64) {
+    const SeqParts sp = sp_first;
+    // A unique key per sequence that orders by decreasing size, then by
+    // increasing sequence index; the rank is the count of larger keys.
+    // Every lane reads all 64 keys from LDS (broadcast reads, no serial
+    // dependency); lanes past S hold -1.
+    const int sz = sp.T - sp.nfull * P;
+    const int key = sp.partial ? (min(sz, (1 << 25) - 1) << 6) | (63 - lane) : -1;
+    scr[128 + lane] = key;
+    lane_exchange_fence();
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; j += 4) {
+      const int4 k4 = *reinterpret_cast<const int4 *>(&scr[128 + j]);
+      rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
+    }
+    lane_exchange_fence();
+    if (sp.partial) scr[64 + rank] = lane;
+    lane_exchange_fence();
+    const int nps = __popcll(__builtin_amdgcn_ballot_w64(sp.partial != 0));
+    NPH = nps * H;
+    const int off = a - F;
+    const bool hit = off >= 0 && off < NPH;
+    const int q = hit ? off / H : 0;
+    const int sel = hit ? scr[64 + q] : lane;
+    const int T_i = __shfl(sp.T, sel, 64), bad_i = __shfl(sp.bad, sel, 64);
+    const int nf_i = __shfl(sp.nfull, sel, 64);
+    if (hit) {
+      c_s = sel;
+      c_h = off - q * H;
+      c_p = nf_i;
+      c_T = T_i;
+      c_bad = bad_i;
+    }
+  } else {
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const SeqParts sp = seq_parts<SPLIT>(p, s0 + lane);
+      const int incl = wave_incl_scan(sp.partial * H, lane);
+      const int tot = __shfl(incl, 63, 64);
+      lane_exchange_fence();
+      scr[lane] = incl;
+      lane_exchange_fence();
+      const int off = a - F - NPH;
+      const bool hit = off >= 0 && off < tot;
+      const int i = hit ? upper_index(scr, off) : lane;
+      const int T_i = __shfl(sp.T, i, 64), bad_i = __shfl(sp.bad, i, 64);
+      const int nf_i = __shfl(sp.nfull, i, 64);
+      if (hit) {
+        c_s = s0 + i;
+        c_h = off - (i ? scr[i - 1] : 0);
+        c_p = nf_i;
+        c_T = T_i;
+        c_bad = bad_i;
+      }
+      NPH += tot;
+    }
+  }
+
+  // Only a unit inside the batch is ever entered.
+  active = c_s >= 0 && c_s < S && c_h >= 0 && c_h < H && c_T >= 0;
+  if (!active) {
+    unit = make_int4(0, 0, 0, 0);
+    bad_part = 0;
+    return;
+  }
+  int lo = 0, hi = c_T;
+  if (SPLIT) {
+    lo = c_p * P;
+    hi = c_T < lo + P ? c_T : lo + P;
+  }
+  unit = make_int4(c_s, c_h, lo, hi);
+  bad_part = c_p * 2 + c_bad;
+}
+
+// Compute units of the current device (cached per device).
+inline int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace persist
+}  // namespace pa

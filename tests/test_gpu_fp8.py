@@ -11,6 +11,8 @@
 * Degenerate cases: empty contexts give zeros, bad block ids and lengths
   poison only their rows, results are deterministic.
 
+FP8 pools: keys [nb][H][bs][d], values transposed per block [nb][H][d][bs].
+
 Input codes of the pools are made by torch's float8_e4m3fn conversion of
 seeded values (an input generator; every expected value is the oracle's)."""
 
@@ -37,8 +39,9 @@ def _codes(x, scale):
 
 
 def _fp8_case(case):
-    """Device tensors of a BF16 decode case with the pools as codes."""
-    kc, vc = _codes(case.key_cache, KS), _codes(case.value_cache, VS)
+    """Device tensors of a BF16 decode case with the pools as codes (the
+    value pool in its transposed block layout [nb][H][d][bs])."""
+    kc, vc = _codes(case.key_cache, KS), _codes(np.swapaxes(case.value_cache, 2, 3), VS)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(G.DEV)
     t = dict(key_cache=torch.from_numpy(kc).to(G.DEV), value_cache=torch.from_numpy(vc).to(G.DEV),
              key=bf(case.key), value=bf(case.value), query=bf(case.query),
@@ -103,7 +106,7 @@ def test_cache_write_fp8_bitexact(in_dtype, hkv, bs, d):
     slots[3] = -1                       # skipped
     slots[7] = nb * bs + 2              # outside the pool: skipped
     kc0 = np.full((nb, hkv, bs, d), 0xA5, np.uint8)
-    vc0 = np.full((nb, hkv, bs, d), 0x5A, np.uint8)
+    vc0 = np.full((nb, hkv, d, bs), 0x5A, np.uint8)     # value blocks transposed
     tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
     dk, dv = torch.from_numpy(kc0).to(G.DEV), torch.from_numpy(vc0).to(G.DEV)
     pa.pa_reshape_and_cache_fp8(torch.from_numpy(key).to(tdt).to(G.DEV),
@@ -126,7 +129,7 @@ def test_copy_blocks_fp8_pools():
     rng = np.random.default_rng(4)
     nb, hkv, bs, d = 40, 4, 16, 256
     kc = rng.integers(0, 256, size=(nb, hkv, bs, d)).astype(np.uint8)
-    vc = rng.integers(0, 256, size=(nb, hkv, bs, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(nb, hkv, d, bs)).astype(np.uint8)
     ids = rng.permutation(nb)
     pairs = np.array([(int(ids[i]), int(ids[10 + i])) for i in range(10)], dtype=np.int32)
     dk, dv = torch.from_numpy(kc).to(G.DEV), torch.from_numpy(vc).to(G.DEV)
@@ -146,6 +149,8 @@ SHAPES = [
     (128, 16, 8, 8, [5, 250]),
     (64, 8, 16, 2, [1, 2, 70]),
     (256, 5, 8, 2, [3, 99]),
+    (256, 16, 32, 4, [2047, 31, 32, 33]),
+    (256, 64, 4, 2, [200, 64]),
 ]
 
 
