@@ -17,6 +17,12 @@ tokens/s (64 new tokens per step), the decode kernel's roofline against
 8 TB/s HBM (its own launches timed with HIP events on the launch stream) and
 the CPU oracle timed on a bounded sample of the same workload.
 
+The FP8 leg ("fp8") repeats the decode step over E4M3FN code pools (the
+same workload's values divided by fixed pool scales; the value pool in its
+transposed block layout): per layer the quantising write, the matrix-core
+FP8 decode and the merge. It reports its own step time and the FP8 kernel's
+roofline (one byte per cached element) and does not enter `value`.
+
 After the decode measurement, a separate leg times the chunked-prefill
 workload (16 sequences with 0-6000 cached tokens, a 512-token causal chunk
 each, 24/4 heads, head_dim 256, BF16, block_size 16): the slot write of the
@@ -40,7 +46,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # and scaled by the same counters' reading for a plain copy of known size.
 TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_persistent_mixed_64seq_hbm_counters.md")
 TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
-                   for f in ("decode_persistent.hip", "pa_device.h")]
+                   for f in ("decode_persistent.hip", "pa_device.h", "persistent_plan.h")]
+FP8_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_fp8_mixed_64seq_hbm_counters.md")
+FP8_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
+                       for f in ("decode_fp8.hip", "pa_device.h", "persistent_plan.h")]
 PREFILL_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "prefill_mfma_chunked_16x512.md")
 PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
                            for f in ("prefill_mfma.hip", "pa_device.h")]
@@ -326,7 +335,7 @@ def loop_leg(seed, steps, dev):
 FP8_SCALES = (0.0375, 0.021)   # k_scale, v_scale of the FP8 pools (N(0,1) data)
 
 
-def fp8_leg(layers, meta, P, steps, warmup, dev):
+def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     """The same decode step over FP8 (E4M3FN) pools: each layer's BF16 pools
     are converted to codes of value / scale before timing (input
     preparation); one step = per layer the quantising write of the step's new
@@ -399,7 +408,9 @@ def fp8_leg(layers, meta, P, steps, warmup, dev):
         "partition_size": P,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned_fp8",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic(workload, P, seed, FP8_TRAFFIC_RECORD,
+                                                FP8_TRAFFIC_SOURCES),
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
@@ -510,7 +521,7 @@ def main():
     if args.fp8:
         del po, pm, ps, outs
         result["fp8"] = fp8_leg(layers, meta, args.fp8_partition_size or P, args.steps,
-                                args.warmup, dev)
+                                args.warmup, dev, W, args.seed)
     if args.prefill_reps > 0:
         del layers
         if not args.fp8:

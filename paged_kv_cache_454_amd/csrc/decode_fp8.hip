@@ -22,9 +22,13 @@
 // Per tile (32 tokens of one KV head: two 16-token halves, each inside one
 // block, 8 KiB of K codes and 8 KiB of V codes):
 //  * K (rows [token][256]) is the A operand of S^T = K . Q^T: lane (m, g)
-//    (m = lane % 16, g = lane / 16) loads 16 bytes of token row m of each
-//    half at byte 16g + 64j, j = 0..3 (four 1 KiB wavefront loads per
-//    half); rows past the context lie outside the load's range and read as
+//    (m = lane % 16, g = lane / 16) needs, for j = 0..3, the 16 bytes of
+//    token row m at byte 16g + 64j. Loaded that way, one wavefront load
+//    would read 64-byte halves of 16 different 128-byte lines; instead each
+//    load reads whole lines of 8 rows (lane (m, g): row 8i + m % 8, byte
+//    128p + 16g + 64 (m / 8)), and a DPP rotation by 8 lanes within each
+//    16-lane row exchanges the halves so that every lane holds its own row's
+//    pieces. Rows past the context lie outside the load's range and read as
 //    zeros. Each 16-byte piece feeds two MFMA steps of 8 channels; the query
 //    fragment of a step (B operand, lane (head n, g)) takes the same
 //    channels 64j + 16g + 8h .. +7, so the contraction pairs every channel
@@ -274,7 +278,9 @@ void decode_fp8_kernel(DecodeParams p) {
     if (r.n1 <= 0) r.b1 = 0;
     return r;
   };
-  const int koff = n16 * D + 16 * grp;  // lane's byte offset in a K half
+  // lane's byte offset in a K half: row m % 8 (+ 8 for the second load of a
+  // pair), byte 16g + 64 (m / 8) (+ 128 for the second pair)
+  const int koff = (n16 & 7) * D + 16 * grp + 64 * (n16 >> 3);
   // lane's byte offset from its V half's base: channel 16 (g >> 1) + c
   const int64_t voff = (int64_t)(16 * (grp >> 1) + n16) * bs;
   auto load_k = [&](u32x4(&kt)[KL], const Desc8 &d) {
@@ -287,8 +293,9 @@ void decode_fp8_kernel(DecodeParams p) {
                                 (int64_t)d.head * head_stride + (int64_t)off * D),
           (short)0, n * D, 0x00020000);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        kt[4 * h + j] = __builtin_amdgcn_raw_buffer_load_b128(r, koff + 64 * j, 0, kStreamLoad);
+      for (int j = 0; j < 4; ++j)  // load 2p + i: bytes 128p.. of rows 8i..8i+7
+        kt[4 * h + j] = __builtin_amdgcn_raw_buffer_load_b128(
+            r, koff + (j & 1) * 8 * D + (j >> 1) * 128, 0, kStreamLoad);
     }
   };
   // V codes: vt[L] holds tokens 0..15 of half g & 1 at channel
@@ -354,7 +361,24 @@ void decode_fp8_kernel(DecodeParams p) {
   const int qh = live_head ? n16 : 0;
 
   // S^T, softmax and the weights (B operand of P.V) for one tile.
-  auto qk_softmax = [&](const u32x4(&kt)[KL], int qslot, int nvalid) -> u32x4 {
+  auto qk_softmax = [&](const u32x4(&kraw)[KL], int qslot, int nvalid) -> u32x4 {
+    // Loads 2p, 2p+1 of a half give lane m < 8 row m's piece j = 2p and lane
+    // m >= 8 row m's piece j = 2p+1; each lane passes the piece its partner
+    // m ^ 8 needs (row rotation by 8) and keeps its own.
+    u32x4 kt[KL];
+    const bool lo8 = n16 < 8;
+#pragma unroll
+    for (int hp = 0; hp < 4; ++hp) {
+      const u32x4 v0 = kraw[2 * hp], v1 = kraw[2 * hp + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t send = lo8 ? v1[w] : v0[w];
+        const uint32_t recv =
+            (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x128, 0xf, 0xf, false);
+        kt[2 * hp][w] = lo8 ? v0[w] : recv;
+        kt[2 * hp + 1][w] = lo8 ? recv : v1[w];
+      }
+    }
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
