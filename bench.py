@@ -47,7 +47,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_persistent_mixed_64seq_hbm_counters.md")
 TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
                    for f in ("decode_persistent.hip", "pa_device.h", "persistent_plan.h")]
-FP8_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_fp8_mixed_64seq_hbm_counters.md")
+FP8_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_fp8_mixed_64seq_16layer.md")
 FP8_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
                        for f in ("decode_fp8.hip", "pa_device.h", "persistent_plan.h")]
 PREFILL_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "prefill_mfma_chunked_16x512.md")

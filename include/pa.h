@@ -234,7 +234,13 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
  * and the bytes decode streams ([P3] KV-cache section: the cache size is
  * linear in the bytes per element; [P2] s.1: decode is bound by memory
  * traffic). The pages fix no quantised format; this one is the library's
- * choice. Pool layout and the block table are as above, element size 1.
+ * choice. The block table and slots mean what they mean above. Layouts
+ * (element size 1):
+ *  key_cache    uint8 [num_blocks][num_kv_heads][block_size][head_dim]  (as above)
+ *  value_cache  uint8 [num_blocks][num_kv_heads][head_dim][block_size]  (each block
+ *               transposed, token index fastest: the tokens of one channel are
+ *               adjacent, so the P.V contraction loads 16 tokens of a channel at once)
+ * pa_copy_blocks copies whole blocks, so it serves these pools unchanged.
  *
  * pa_reshape_and_cache_fp8 - the slot-mapped write of pa_reshape_and_cache,
  * quantising on the way: the code stored for element x of key (value) is
