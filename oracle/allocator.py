@@ -42,6 +42,36 @@ rollouts diverge). Readings where the page leaves the mechanics open:
 * The recorded copies are taken by the caller once per step and applied to the
   cache pools before that step's writes; the copy itself is the bitwise block
   copy in ``attention.copy_blocks``.
+
+Swapping to host memory ("Inside vLLM: Anatomy of a High-Throughput LLM
+Inference System", section "Memory-Efficient KV Cache Storage": blocks move
+between GPU and CPU memory, and when GPU memory runs short some blocks are
+paged out to host memory; its "How It Works" list: paged attention swaps
+blocks in and out as needed; "The Scheduler: Dynamic Batching & Resource
+Allocation": under memory pressure low-priority requests are suspended).
+Readings where the page leaves the mechanics open:
+* A second, host-side pool of blocks with its own first-in first-out free
+  queue (identity order unless given).
+* The unit of a swap is a whole sequence (a suspended request). Swapping out
+  takes one host block per device block of the sequence, from the front of
+  the host queue, in logical order, and returns the (device block, host
+  block) copies to make; then each device block drops one holder count and
+  the blocks no one else holds go to the back of the device queue in logical
+  order, exactly as in a release. A block shared with another sequence stays
+  on the device for that sequence; the swapped sequence takes its own copy.
+* Swapping in takes one device block per host block from the front of the
+  device queue, in logical order, returns the (host block, device block)
+  copies, and puts the host blocks at the back of the host queue in logical
+  order. Sharing lost at swap-out is not restored.
+* Either direction is all or nothing: too few free blocks on the receiving
+  side raises the out-of-blocks error and changes nothing.
+* A swapped-out sequence keeps its length; it cannot be appended to, forked
+  or exported to a block table until it is swapped back in; releasing it
+  returns its host blocks to the back of the host queue.
+* Copies are applied by the caller: the copy-on-write copies taken before a
+  swap-out are applied before its copies (they may fill the blocks it
+  reads); the swap copies are the bitwise block copy between pools in
+  ``attention.swap_blocks``.
 """
 
 from collections import deque
@@ -54,12 +84,21 @@ class OutOfBlocks(Exception):
 class BlockAllocatorModel:
     """Free-block queue plus one growing block table per sequence."""
 
-    def __init__(self, num_blocks, block_size, initial_order=None):
+    def __init__(self, num_blocks, block_size, initial_order=None, num_host_blocks=0,
+                 host_initial_order=None):
         if initial_order is None:
             initial_order = range(num_blocks)
         order = [int(b) for b in initial_order]
         if sorted(order) != list(range(num_blocks)):
             raise ValueError("initial_order must be a permutation of 0..num_blocks-1")
+        if host_initial_order is None:
+            host_initial_order = range(num_host_blocks)
+        host_order = [int(b) for b in host_initial_order]
+        if sorted(host_order) != list(range(num_host_blocks)):
+            raise ValueError("host_initial_order must be a permutation of 0..num_host_blocks-1")
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_free = deque(host_order)
+        self.host_tables = {}  # swapped-out seq_id -> host block ids, logical order
         self.block_size = int(block_size)
         self.num_blocks = int(num_blocks)
         self.free_blocks = deque(order)
@@ -75,7 +114,7 @@ class BlockAllocatorModel:
         """Start ``child_id`` as a sharer of every block of ``parent_id``."""
         if parent_id not in self.tables:
             raise KeyError(parent_id)
-        if child_id in self.tables:
+        if child_id in self.tables or child_id in self.host_tables:
             raise ValueError(f"sequence {child_id} already exists")
         self.tables[child_id] = list(self.tables[parent_id])
         self.lengths[child_id] = self.lengths[parent_id]
@@ -94,6 +133,8 @@ class BlockAllocatorModel:
         the position in the flattened pool where the token's K and V rows live.
         New blocks are taken only when the current last block is full.
         """
+        if seq_id in self.host_tables:
+            raise ValueError(f"sequence {seq_id} is swapped out")
         held = self.lengths.get(seq_id, 0)
         table = self.tables.get(seq_id, [])
         have = len(table)
@@ -124,15 +165,25 @@ class BlockAllocatorModel:
 
     def free(self, seq_id):
         """Release ``seq_id``: its blocks that no other table holds go to the
-        back of the free queue (in logical order)."""
+        back of the free queue (in logical order); a swapped-out sequence's
+        host blocks go to the back of the host queue."""
+        if seq_id in self.host_tables:
+            self.host_free.extend(self.host_tables.pop(seq_id))
+            del self.lengths[seq_id]
+            return
         if seq_id not in self.tables:
             raise KeyError(seq_id)
-        for b in self.tables.pop(seq_id):
+        self._release(self.tables.pop(seq_id))
+        del self.lengths[seq_id]
+
+    def _release(self, table):
+        """Drop one holder count from each block of ``table``; blocks no
+        table holds any more go to the back of the free queue, in order."""
+        for b in table:
             self.refs[b] -= 1
             if self.refs[b] == 0:
                 del self.refs[b]
                 self.free_blocks.append(b)
-        del self.lengths[seq_id]
 
     def block_table(self, seq_ids, max_blocks, pad=-1):
         """Rows of the block table for ``seq_ids``, padded with ``pad``, and
@@ -145,3 +196,38 @@ class BlockAllocatorModel:
             rows.append(list(t) + [pad] * (max_blocks - len(t)))
             lens.append(self.lengths[sid])
         return rows, lens
+
+    def num_free_host(self):
+        return len(self.host_free)
+
+    def swap_out(self, seq_id):
+        """Move ``seq_id`` to host blocks; returns the (device block, host
+        block) copies to make, in logical order."""
+        if seq_id not in self.tables:
+            raise KeyError(seq_id)
+        table = self.tables[seq_id]
+        if len(table) > len(self.host_free):
+            raise OutOfBlocks(f"sequence {seq_id}: needs {len(table)} host blocks, "
+                              f"{len(self.host_free)} free")
+        host = [self.host_free.popleft() for _ in table]
+        pairs = list(zip(table, host))
+        self._release(self.tables.pop(seq_id))
+        self.host_tables[seq_id] = host
+        return pairs
+
+    def swap_in(self, seq_id):
+        """Bring ``seq_id`` back to device blocks; returns the (host block,
+        device block) copies to make, in logical order."""
+        if seq_id not in self.host_tables:
+            raise KeyError(seq_id)
+        host = self.host_tables[seq_id]
+        if len(host) > len(self.free_blocks):
+            raise OutOfBlocks(f"sequence {seq_id}: needs {len(host)} blocks, "
+                              f"{len(self.free_blocks)} free")
+        table = [self.free_blocks.popleft() for _ in host]
+        for b in table:
+            self.refs[b] = 1
+        pairs = list(zip(host, table))
+        self.host_free.extend(self.host_tables.pop(seq_id))
+        self.tables[seq_id] = table
+        return pairs

@@ -71,6 +71,24 @@ def copy_blocks(key_cache, value_cache, block_pairs):
     return kc, vc
 
 
+def swap_blocks(src_key, src_value, dst_key, dst_value, block_pairs):
+    """Block moves between two pools of the same block shape ("Inside vLLM:
+    Anatomy of a High-Throughput LLM Inference System", "Memory-Efficient KV
+    Cache Storage": blocks are paged out to host memory and back): for each
+    (src, dst) pair, every KV head and token row of block src of the source
+    pools is written to block dst of copies of the destination pools. Pairs
+    whose ids fall outside their pool are skipped. A bit copy."""
+    kd = dst_key.copy()
+    vd = dst_value.copy()
+    ns, nd = src_key.shape[0], dst_key.shape[0]
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        if not (0 <= src < ns and 0 <= dst < nd):
+            continue
+        kd[dst] = src_key[src]
+        vd[dst] = src_value[src]
+    return kd, vd
+
+
 def gather_context(cache, block_table_row, context_len, block_size):
     """Logical [context_len][num_kv_heads][head_dim] view of one sequence's
     cache, rebuilt position by position through its block table."""

@@ -318,6 +318,154 @@ def pin_cow_counts(alloc):
             assert b.num_free() - before == 1 + (2 if c == k else 0)
 
 
+def _swap_state_ok(a):
+    _cow_state_ok(a)
+    host_held = [b for t in a.host_tables.values() for b in t]
+    assert len(host_held) == len(set(host_held))          # a host block has one owner
+    assert not set(host_held) & set(a.host_free)
+    assert len(host_held) + a.num_free_host() == a.num_host_blocks
+    assert not set(a.host_tables) & set(a.tables)
+
+
+def pin_swap_contents(alloc):
+    """Swapping judged by what each sequence reads back: the copy-on-write
+    simulation above with a host pool beside the device pool. Swap-out pairs
+    move device blocks to host blocks and swap-in pairs move them back (after
+    the step's copy-on-write copies); every resident sequence reads its own
+    history through its table from the device pool, every swapped-out one
+    through its host blocks from the host pool."""
+    rng = random.Random(23)
+    for bs, nb, nh in ((4, 40, 24), (1, 24, 30), (3, 36, 12)):
+        a = alloc.BlockAllocatorModel(nb, bs, num_host_blocks=nh)
+        dev = [[None] * bs for _ in range(nb)]
+        host = [[None] * bs for _ in range(nh)]
+        history, swapped = {}, set()
+        mark = 0
+        for _ in range(700):
+            op = rng.random()
+            live = sorted(s for s in history if s not in swapped)
+            out = sorted(swapped)
+            if op < 0.4 or not history:
+                sid = rng.choice(live) if live and rng.random() < 0.8 else rng.randrange(1000)
+                if sid in history and sid in swapped:
+                    continue
+                n = rng.randint(0, 2 * bs + 1)
+                try:
+                    slots = a.append(sid, n)
+                except alloc.OutOfBlocks:
+                    assert a.take_copies() == []
+                    continue
+                for src, dst in a.take_copies():
+                    dev[dst] = list(dev[src])
+                for slot in slots:
+                    mark += 1
+                    dev[slot // bs][slot % bs] = mark
+                    history.setdefault(sid, []).append(mark)
+                history.setdefault(sid, [])
+            elif op < 0.55 and live:
+                parent = rng.choice(live)
+                child = 1000 + rng.randrange(1000)
+                if child in history:
+                    continue
+                a.fork(parent, child)
+                history[child] = list(history[parent])
+            elif op < 0.7 and live:
+                sid = rng.choice(live)
+                free_before = (a.num_free(), a.num_free_host())
+                table = list(a.tables[sid])
+                try:
+                    pairs = a.swap_out(sid)
+                except alloc.OutOfBlocks:
+                    assert (a.num_free(), a.num_free_host()) == free_before
+                    continue
+                assert [d for d, _ in pairs] == table        # every block, logical order
+                for d, h in pairs:
+                    host[h] = list(dev[d])
+                swapped.add(sid)
+            elif op < 0.85 and out:
+                sid = rng.choice(out)
+                free_before = (a.num_free(), a.num_free_host())
+                try:
+                    pairs = a.swap_in(sid)
+                except alloc.OutOfBlocks:
+                    assert (a.num_free(), a.num_free_host()) == free_before
+                    continue
+                for h, d in pairs:
+                    dev[d] = list(host[h])
+                swapped.discard(sid)
+            else:
+                sid = rng.choice(sorted(history))
+                a.free(sid)
+                del history[sid]
+                swapped.discard(sid)
+            for sid, hist in history.items():
+                assert a.lengths[sid] == len(hist)
+                if sid in swapped:
+                    t = a.host_tables[sid]
+                    assert [host[t[p // bs]][p % bs] for p in range(len(hist))] == hist, sid
+                else:
+                    t = a.tables[sid]
+                    assert [dev[t[p // bs]][p % bs] for p in range(len(hist))] == hist, sid
+            _swap_state_ok(a)
+
+
+def pin_swap_counts(alloc):
+    """Swap order and atomicity on a small pool, every block id fixed by the
+    first-in first-out queues: swap-out takes host blocks from the front in
+    logical order and frees the device blocks no one else holds to the back;
+    swap-in does the reverse; a side without room raises and changes nothing;
+    a swapped-out sequence cannot grow or be forked and keeps its length."""
+    a = alloc.BlockAllocatorModel(16, 4, num_host_blocks=6)
+    a.append(0, 10)                                      # device 0, 1, 2
+    a.append(1, 5)                                       # device 3, 4
+    assert a.swap_out(0) == [(0, 0), (1, 1), (2, 2)]
+    assert list(a.free_blocks) == list(range(5, 16)) + [0, 1, 2]
+    assert a.num_free_host() == 3 and a.lengths[0] == 10
+    assert a.swap_out(1) == [(3, 3), (4, 4)]
+    assert list(a.free_blocks)[-2:] == [3, 4] and list(a.host_free) == [5]
+    for bad in (lambda: a.append(0, 1), lambda: a.fork(0, 9), lambda: a.block_table([0], 4)):
+        try:
+            bad()
+        except (ValueError, KeyError):
+            pass
+        else:
+            raise AssertionError("a swapped-out sequence was used")
+    a.append(2, 6)                                       # device 5, 6 (6 half full)
+    a.fork(2, 3)
+    snap = (list(a.free_blocks), list(a.host_free), dict(a.refs), dict(a.host_tables))
+    try:
+        a.swap_out(3)                                    # needs 2 host blocks, 1 free
+    except alloc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("swap-out beyond the host pool")
+    assert snap == (list(a.free_blocks), list(a.host_free), dict(a.refs), dict(a.host_tables))
+    a.free(1)                                            # host 3, 4 back at the end
+    assert list(a.host_free) == [5, 3, 4]
+    assert a.swap_out(3) == [(5, 5), (6, 3)]             # shared blocks stay for 2
+    assert a.refs == {5: 1, 6: 1} and 5 not in a.free_blocks
+    assert a.swap_in(0) == [(0, 7), (1, 8), (2, 9)]
+    assert list(a.host_free) == [4, 0, 1, 2] and a.tables[0] == [7, 8, 9]
+    assert a.append(0, 2) == [9 * 4 + 2, 9 * 4 + 3]        # grows in its new last block
+    b = alloc.BlockAllocatorModel(4, 2, num_host_blocks=8)
+    b.append(0, 6)                                       # device 0, 1, 2
+    b.swap_out(0)
+    b.append(1, 4)                                       # device 3, 0
+    snap = (list(b.free_blocks), list(b.host_free), dict(b.refs))
+    try:
+        b.swap_in(0)                                     # needs 3, 2 free
+    except alloc.OutOfBlocks:
+        pass
+    else:
+        raise AssertionError("swap-in beyond the device pool")
+    assert snap == (list(b.free_blocks), list(b.host_free), dict(b.refs))
+    b.free(1)
+    assert b.swap_in(0) == [(0, 1), (1, 2), (2, 3)]
+    assert b.block_table([0], 3) == ([[1, 2, 3]], [6])
+    b.free(0)
+    assert list(b.host_free) == [3, 4, 5, 6, 7, 0, 1, 2] and b.num_free() == 4
+
+
 # -------------------------------------------------------------- attention
 
 def pin_cache_write(attn):
@@ -500,6 +648,31 @@ def pin_prefill(attn):
             assert np.abs(out[qsl[s] + j] - want).max() < 1e-12
 
 
+def pin_swap_blocks(attn):
+    """Block moves between two pools of different sizes against element-wise
+    loops: each destination block equals its source block in all heads and
+    rows, the source pools and all other destination blocks are untouched,
+    and pairs out of either pool's range change nothing."""
+    rng = np.random.default_rng(6)
+    sk, sv = rng.standard_normal((5, 2, 3, 4)), rng.standard_normal((5, 2, 3, 4))
+    dk, dv = rng.standard_normal((8, 2, 3, 4)), rng.standard_normal((8, 2, 3, 4))
+    sk0, sv0 = sk.copy(), sv.copy()
+    pairs = [(4, 0), (0, 7), (2, 3), (5, 1), (1, 8), (-1, 2)]
+    k2, v2 = attn.swap_blocks(sk, sv, dk, dv, pairs)
+    src_of = {0: 4, 7: 0, 3: 2}
+    for b in range(8):
+        for h in range(2):
+            for r in range(3):
+                for c in range(4):
+                    if b in src_of:
+                        assert k2[b, h, r, c] == sk[src_of[b], h, r, c]
+                        assert v2[b, h, r, c] == sv[src_of[b], h, r, c]
+                    else:
+                        assert k2[b, h, r, c] == dk[b, h, r, c]
+                        assert v2[b, h, r, c] == dv[b, h, r, c]
+    assert np.array_equal(sk, sk0) and np.array_equal(sv, sv0)
+
+
 def pin_copy_blocks(attn):
     """Block copies against element-wise loops over a pool of distinct
     values: every destination block equals its source in all heads and rows,
@@ -612,8 +785,8 @@ def attention_decode_ref(q, kc, vc, tables, lens, bs, scale, v_tokens_last=False
 
 ATTENTION_PINS = [pin_cache_write, pin_decode_bruteforce, pin_decode_vs_library,
                   pin_decode_special_cases, pin_permutation_invariance, pin_partitions,
-                  pin_prefill, pin_copy_blocks]
+                  pin_prefill, pin_copy_blocks, pin_swap_blocks]
 ACCOUNTING_PINS = [pin_kv_size, pin_worked_example_accounting]
 FP8_PINS = [pin_fp8_codes, pin_fp8_cache]
 ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants, pin_cow_contents,
-                  pin_cow_counts]
+                  pin_cow_counts, pin_swap_contents, pin_swap_counts]

@@ -83,6 +83,27 @@ MUTATIONS += [
     ("fp8", "    return kc, value_pool(vr)", "    return kc, vr"),
 ]
 
+MUTATIONS += [
+    ("allocator", "        host = [self.host_free.popleft() for _ in table]",
+     "        host = [self.host_free.pop() for _ in table]"),
+    ("allocator", "        table = [self.free_blocks.popleft() for _ in host]",
+     "        table = [self.free_blocks.pop() for _ in host]"),
+    ("allocator", "        pairs = list(zip(table, host))", "        pairs = list(zip(host, table))"),
+    ("allocator", "        pairs = list(zip(host, table))", "        pairs = list(zip(table, host))"),
+    ("allocator", "        if len(table) > len(self.host_free):",
+     "        if len(table) > len(self.host_free) + 1:"),
+    ("allocator", "        if len(host) > len(self.free_blocks):",
+     "        if len(host) - 1 > len(self.free_blocks):"),
+    ("allocator", "        self.host_free.extend(self.host_tables.pop(seq_id))\n        self.tables[seq_id] = table",
+     "        self.host_tables.pop(seq_id)\n        self.tables[seq_id] = table"),
+    ("allocator", "        self._release(self.tables.pop(seq_id))\n        self.host_tables[seq_id] = host",
+     "        self.free_blocks.extend(self.tables.pop(seq_id))\n        self.host_tables[seq_id] = host"),
+    ("attention", "        kd[dst] = src_key[src]", "        kd[dst] = src_key[dst % ns]"),
+    ("attention", "        vd[dst] = src_value[src]", "        vd[dst] = src_key[src]"),
+    ("attention", "        if not (0 <= src < ns and 0 <= dst < nd):\n            continue\n        kd[dst]",
+     "        if not (0 <= src < nd and 0 <= dst < ns):\n            continue\n        kd[dst]"),
+]
+
 PINS = {"attention": P.ATTENTION_PINS, "accounting": P.ACCOUNTING_PINS,
         "allocator": P.ALLOCATOR_PINS, "fp8": P.FP8_PINS}
 
