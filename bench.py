@@ -27,7 +27,10 @@ After the decode measurement, a separate leg times the chunked-prefill
 workload (16 sequences with 0-6000 cached tokens, a 512-token causal chunk
 each, 24/4 heads, head_dim 256, BF16, block_size 16): the slot write of the
 chunk's K/V and pa_prefill_chunk, the latter against the BF16 matrix-core
-peak. It reports under "prefill" and does not enter `value`.
+peak. It reports under "prefill" and does not enter `value`. Two more side
+legs time block moves: "cow" (copy-on-write clones of a 16-rollout fan-out,
+pa_copy_blocks, against HBM) and "swap" (8 sequences preempted to pinned
+host memory and brought back, pa_swap_blocks, against the PCIe link).
 """
 
 import argparse
@@ -262,6 +265,71 @@ def cow_leg(seed, reps, dev):
                      "traffic": None},
         "steps": reps,
     }
+
+
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16 host link, per direction, nominal
+
+
+def swap_leg(seed, reps, dev):
+    """Swapping to host memory: 8 of the mixed workload's 64 sequences
+    (seeded choice) are preempted - the native allocator moves their blocks
+    to a pinned host pool - and brought back into fresh device blocks. Each
+    direction applies its block moves to the pools of all 16 layers (4 KV
+    heads x 16 tokens x 256, BF16) with one pa_swap_blocks launch per layer:
+    the kernel reads HBM and writes host memory over the bus (swap-out), or
+    the reverse (swap-in)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    from paged_kv_cache_454_amd import BlockAllocator, inputs
+    lens = [int(x) for x in inputs.preset_lengths("mixed", seed)]
+    bs, hkv, d, nlayers = 16, 4, 256, 16
+    victims = sorted(int(v) for v in np.random.default_rng(seed + 2).choice(len(lens), 8,
+                                                                           replace=False))
+    nb = sum(-(-n // bs) for n in lens) + 16
+    nh = sum(-(-lens[v] // bs) for v in victims)
+    a = BlockAllocator(nb, bs)
+    a.set_host_pool(nh)
+    for s, n in enumerate(lens):
+        a.append(s, n)
+    out_pairs = np.concatenate([a.swap_out(v) for v in victims])
+    in_pairs = np.concatenate([a.swap_in(v) for v in victims])
+    dev_pools = [(torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev),
+                  torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev))
+                 for _ in range(nlayers)]
+    host_pools = [(torch.zeros((nh, hkv, bs, d), dtype=torch.bfloat16, pin_memory=True),
+                   torch.zeros((nh, hkv, bs, d), dtype=torch.bfloat16, pin_memory=True))
+                  for _ in range(nlayers)]
+    po, pi = torch.from_numpy(out_pairs).to(dev), torch.from_numpy(in_pairs).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def swap_out():
+        for (dk, dv), (hk, hv) in zip(dev_pools, host_pools):
+            pa.pa_swap_blocks(dk, dv, hk, hv, po, stream=stream)
+
+    def swap_in():
+        for (dk, dv), (hk, hv) in zip(dev_pools, host_pools):
+            pa.pa_swap_blocks(hk, hv, dk, dv, pi, stream=stream)
+
+    swap_out()
+    swap_in()
+    torch.cuda.synchronize()
+    block_bytes = hkv * bs * d * 2
+    res = {"workload": f"preempt 8 of the 64 mixed-length sequences ({nh} blocks of 4 x 16 x "
+                       f"256 BF16) to pinned host memory and back, 16 layers",
+           "sequences": victims, "pairs": int(len(out_pairs)), "steps": reps}
+    for name, fn in (("out", swap_out), ("in", swap_in)):
+        ms = timed_launches(fn, reps, stream) / nlayers
+        nbytes = 2 * len(out_pairs) * block_bytes        # K and V blocks crossing the link
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bytes_per_launch": nbytes, "us_per_launch": round(ms * 1e3, 2),
+                     "roofline": {"bound": "pcie", "kernel": "pa_swap_blocks",
+                                  "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / PCIE_PEAK_GBS, 4),
+                                  "traffic": None}}
+    del dev_pools, host_pools
+    return res
 
 
 def loop_leg(seed, steps, dev):
@@ -529,6 +597,7 @@ def main():
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)
+        result["swap"] = swap_leg(args.seed, args.prefill_reps, dev)
     if args.loop_steps > 0:
         result["loop"] = loop_leg(args.seed, args.loop_steps, dev)
     if args.cpu_seconds > 0 and W == "mixed":

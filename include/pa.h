@@ -13,8 +13,8 @@
  *       Continuous Batching" (voronkin.com), KV-cache and PagedAttention
  *       sections.
  *  [P4] "Inside vLLM: Anatomy of a High-Throughput LLM Inference System"
- *       (syntaxis blog), "Garbage Collection & Reuse", "FlashAttention-2
- *       Integration".
+ *       (syntaxis blog), "Memory-Efficient KV Cache Storage", "Garbage
+ *       Collection & Reuse", "FlashAttention-2 Integration".
  *
  * Conventions shared by every device entry point
  * ----------------------------------------------
@@ -64,8 +64,8 @@ typedef enum pa_status {
   PA_ENOTFOUND = 5      /* allocator: unknown sequence id                    */
 } pa_status;
 
-/* PA_FP8_E4M3: one-byte OCP E4M3FN codes (pools of the *_fp8 entry points
- * and pa_copy_blocks only; see pa_reshape_and_cache_fp8). */
+/* PA_FP8_E4M3: one-byte OCP E4M3FN codes (pools of the *_fp8 entry points,
+ * pa_copy_blocks and pa_swap_blocks only; see pa_reshape_and_cache_fp8). */
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Message describing the last non-OK status returned on this thread
@@ -113,6 +113,39 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *bloc
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype kv_dtype,
                          hipStream_t stream);
+
+/*
+ * pa_swap_blocks - move whole blocks between two pairs of pools, one of which
+ * is usually in pinned host memory ([P4] "Memory-Efficient KV Cache Storage":
+ * blocks move between GPU and CPU memory; when GPU memory runs short they are
+ * paged out to host memory; pa_alloc_swap_out / pa_alloc_swap_in list the
+ * pairs). For each pair, block src of the source pools (all num_kv_heads x
+ * block_size rows, both pools) is copied to block dst of the destination
+ * pools; the copy runs in one kernel that reads or writes the host side over
+ * the bus.
+ *  src_key_cache,
+ *  src_value_cache  [device or pinned host] kv_dtype [src_num_blocks][...]
+ *  dst_key_cache,
+ *  dst_value_cache  [device or pinned host] kv_dtype [dst_num_blocks][...],
+ *                   updated in place
+ *  block_pairs      [device or pinned host] int32 [num_pairs][2] = (src, dst)
+ * Pool layouts as above (FP8 pools included: a block is copied whole, so the
+ * transposed value layout needs nothing special). "Pinned host" means memory
+ * from hipHostMalloc (torch's pin_memory=True), which the device addresses
+ * at the same pointer; every buffer's first and last byte are checked and
+ * anything else (pageable memory, another device's memory) gives PA_EINVAL
+ * before any launch. A pair with an id outside its pool is skipped; when
+ * source and destination are the same pools a pair with src == dst is too.
+ * Destinations must be distinct and, for the same pools, never a source.
+ * A bit copy, asynchronous on stream: the host side must stay allocated and
+ * untouched by the host until the stream has passed the copy.
+ * num_pairs == 0 is a no-op.
+ */
+pa_status pa_swap_blocks(const void *src_key_cache, const void *src_value_cache,
+                         int32_t src_num_blocks, void *dst_key_cache, void *dst_value_cache,
+                         int32_t dst_num_blocks, const int32_t *block_pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype kv_dtype, hipStream_t stream);
 
 /*
  * pa_decode - single-pass paged decode attention: one query token per
@@ -339,7 +372,7 @@ int32_t pa_alloc_take_copies(pa_alloc *a, int32_t *pairs_out, int32_t max_pairs)
 /* Number of sequences holding block (0 = free), or -1 if out of range. */
 int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block);
 
-/* One step of an iteration-level decode loop ([W2] s.3 "Continuous
+/* One step of an iteration-level decode loop ([P2] s.3 "Continuous
  * Batching": every iteration each running sequence gets its next token, and
  * finished ones leave at once), in one call: append num_tokens[i] tokens to
  * seq_ids[i] for i < n (as pa_alloc_append, copy on write included), then
@@ -358,6 +391,48 @@ int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block);
 pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const int32_t *num_tokens, int32_t n,
                         int64_t *slots_out, int32_t max_blocks, int32_t *table_out,
                         int32_t *lens_out);
+
+/* Swapping to host memory ([P4] "Memory-Efficient KV Cache Storage": when
+ * GPU memory runs short, blocks are paged out to host memory; "The
+ * Scheduler": requests are suspended under memory pressure). The unit is a
+ * whole sequence.
+ *
+ * pa_alloc_set_host_pool - give the allocator a host pool of num_host_blocks
+ * blocks (ids 0..num_host_blocks-1) with its own first-in first-out free
+ * queue in initial_order ([host] int32 [num_host_blocks], a permutation, or
+ * NULL = 0, 1, 2, ...). Replaces any earlier host pool; PA_EINVAL while a
+ * sequence is swapped out. Without a call the host pool is empty. */
+pa_status pa_alloc_set_host_pool(pa_alloc *a, int32_t num_host_blocks,
+                                 const int32_t *initial_order);
+
+/* Free blocks of the host pool; -1 if a is NULL. */
+int32_t pa_alloc_num_free_host(const pa_alloc *a);
+
+/* 1 if seq_id is swapped out, 0 if it is on device blocks, -1 if unknown. */
+int32_t pa_alloc_is_swapped(const pa_alloc *a, int64_t seq_id);
+
+/* pa_alloc_swap_out - move seq_id to host blocks: one host block per device
+ * block, from the front of the host queue, in logical order; then the device
+ * blocks are released as by pa_alloc_free (a block another table holds stays
+ * with it). pairs_out [host] int32 [max_pairs][2] receives the (device block,
+ * host block) moves in logical order, *num_pairs their count (the sequence's
+ * block count, ceil(len / block_size)). Apply them with pa_swap_blocks
+ * (device pools -> host pools) after any copy-on-write pairs taken before the
+ * call and before the freed device blocks are written again.
+ * pa_alloc_swap_in - the reverse: one device block per host block from the
+ * front of the device queue; pairs_out receives (host block, device block);
+ * the host blocks go to the back of the host queue. Blocks shared before a
+ * swap-out come back as the sequence's own.
+ * Both are all or nothing: PA_ENOMEM if the receiving side has too few free
+ * blocks, PA_EINVAL if max_pairs is too small or the sequence is already on
+ * that side, PA_ENOTFOUND for an unknown id; nothing changes then. A
+ * swapped-out sequence keeps its length; pa_alloc_append, pa_alloc_fork,
+ * pa_alloc_step and pa_alloc_block_table refuse it (PA_EINVAL) and
+ * pa_alloc_free returns its host blocks to the back of the host queue. */
+pa_status pa_alloc_swap_out(pa_alloc *a, int64_t seq_id, int32_t max_pairs, int32_t *pairs_out,
+                            int32_t *num_pairs);
+pa_status pa_alloc_swap_in(pa_alloc *a, int64_t seq_id, int32_t max_pairs, int32_t *pairs_out,
+                           int32_t *num_pairs);
 
 /* Free blocks in the pool; -1 if a is NULL. */
 int32_t pa_alloc_num_free(const pa_alloc *a);

@@ -52,6 +52,12 @@ SIGNATURES = {
     "pa_alloc_take_copies": (_i32, [_p, _p, _i32]),
     "pa_alloc_block_refs": (_i32, [_p, _i32]),
     "pa_alloc_step": (_st, [_p, _p, _p, _i32, _p, _i32, _p, _p]),
+    "pa_swap_blocks": (_st, [_p, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _st, _p]),
+    "pa_alloc_set_host_pool": (_st, [_p, _i32, _p]),
+    "pa_alloc_num_free_host": (_i32, [_p]),
+    "pa_alloc_is_swapped": (_i32, [_p, _i64]),
+    "pa_alloc_swap_out": (_st, [_p, _i64, _i32, _p, _p]),
+    "pa_alloc_swap_in": (_st, [_p, _i64, _i32, _p, _p]),
 }
 
 _LIB = None

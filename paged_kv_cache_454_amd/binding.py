@@ -101,6 +101,45 @@ def pa_copy_blocks(key_cache, value_cache, block_pairs, stream=None):
                                num_blocks, dt, _stream(stream)))
 
 
+def _reachable(t, what, dtype=None):
+    """Pointer of a contiguous tensor in device memory or pinned host memory
+    (the library checks that the device can address it)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{what}: must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if t.data_ptr() % 16 != 0 and t.numel() > 0:
+        raise ValueError(f"{what}: data pointer must be 16-byte aligned")
+    return t.data_ptr()
+
+
+def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, block_pairs,
+                   stream=None):
+    """Copy whole blocks from the source pools to the destination pools, one
+    side usually pinned host memory (swap-out: device -> host; swap-in: host
+    -> device). block_pairs: int32 [n][2] (source id, destination id), on the
+    device or pinned."""
+    fp8 = src_key_cache.dtype in _FP8
+    shape = _fp8_pool_shape if fp8 else _pool_shape
+    snb, hkv, bs, d = shape(src_key_cache, src_value_cache)
+    dnb, hkv2, bs2, d2 = shape(dst_key_cache, dst_value_cache)
+    if (hkv, bs, d) != (hkv2, bs2, d2) or src_key_cache.dtype != dst_key_cache.dtype:
+        raise ValueError("source and destination pools must have the same block shape and dtype")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [num_pairs][2]")
+    dt = PA_FP8_E4M3 if fp8 else _dtype(src_key_cache, "pools")
+    check(lib().pa_swap_blocks(
+        _reachable(src_key_cache, "src_key_cache"), _reachable(src_value_cache, "src_value_cache"),
+        snb, _reachable(dst_key_cache, "dst_key_cache"),
+        _reachable(dst_value_cache, "dst_value_cache"), dnb,
+        _reachable(block_pairs, "block_pairs", torch.int32), block_pairs.shape[0], hkv, d, bs,
+        dt, _stream(stream)))
+
+
 def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
                              stream=None):
     """Quantising write: the E4M3 codes of key / k_scale and value / v_scale
@@ -322,6 +361,39 @@ class BlockAllocator:
 
     def block_refs(self, block):
         return int(lib().pa_alloc_block_refs(self._h, int(block)))
+
+    def set_host_pool(self, num_host_blocks, initial_order=None):
+        """Give the allocator a host pool with its own FIFO free queue."""
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.shape != (num_host_blocks,):
+                raise ValueError("initial_order must have num_host_blocks entries")
+        check(lib().pa_alloc_set_host_pool(self._h, int(num_host_blocks),
+                                           None if order is None else order.ctypes.data))
+
+    def num_free_host(self):
+        return int(lib().pa_alloc_num_free_host(self._h))
+
+    def is_swapped(self, seq_id):
+        return int(lib().pa_alloc_is_swapped(self._h, int(seq_id)))
+
+    def _swap(self, fn, seq_id):
+        n_blocks = -(-max(self.seq_len(seq_id), 0) // self.block_size)
+        pairs = np.empty((max(n_blocks, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        check(fn(self._h, int(seq_id), n_blocks, pairs.ctypes.data, ctypes.byref(n)))
+        return pairs[:n.value]
+
+    def swap_out(self, seq_id):
+        """Move a sequence to host blocks; returns int32 [n][2] (device block,
+        host block) moves for pa_swap_blocks."""
+        return self._swap(lib().pa_alloc_swap_out, seq_id)
+
+    def swap_in(self, seq_id):
+        """Bring a sequence back to device blocks; returns int32 [n][2] (host
+        block, device block) moves for pa_swap_blocks."""
+        return self._swap(lib().pa_alloc_swap_in, seq_id)
 
     def step(self, seq_ids, num_tokens, max_blocks, slots_out=None, table_out=None,
              lens_out=None):

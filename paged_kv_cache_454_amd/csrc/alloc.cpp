@@ -21,6 +21,18 @@
 // queue, records the pending copy (old -> fresh) and swaps it in; a release
 // returns only the blocks whose count drops to zero. Full shared blocks are
 // never written again (sequences only grow), so they stay shared.
+//
+// Swapping to host memory ("Inside vLLM: Anatomy of a High-Throughput LLM
+// Inference System", "Memory-Efficient KV Cache Storage": when GPU memory runs
+// short, blocks are paged out to host memory and later brought back). A
+// second ring holds the free blocks of a host pool. A swap moves a whole
+// sequence: swap-out takes one host block per device block from the front of
+// the host queue and releases the device blocks as a free would (blocks
+// another table holds stay); swap-in takes one device block per host block
+// from the front of the device queue and returns the host blocks to the back
+// of theirs. Both are all or nothing and hand back the block moves the
+// caller applies with pa_swap_blocks. While swapped out a sequence keeps its
+// length but cannot grow, fork or be exported to a block table.
 #include <cstdint>
 #include <new>
 #include <unordered_map>
@@ -28,30 +40,43 @@
 
 #include "pa_internal.h"
 
-struct pa_alloc {
-  int32_t num_blocks = 0;
-  int32_t block_size = 0;
-  std::vector<int32_t> ring;  // free queue storage, capacity num_blocks
-  int64_t head = 0;           // index of the front element
-  int64_t count = 0;          // elements in the queue
-  std::vector<int32_t> refs;  // tables holding each block (0 = free)
-  std::vector<int32_t> copies;  // pending (source, destination) pairs, flattened
-  struct Seq {
-    std::vector<int32_t> blocks;
-    int64_t len = 0;
-  };
-  std::unordered_map<int64_t, Seq> seqs;
+// A first-in first-out queue of block ids in a ring of fixed capacity.
+struct BlockRing {
+  std::vector<int32_t> ring;
+  int64_t head = 0;   // index of the front element
+  int64_t count = 0;  // elements in the queue
 
   int32_t pop_front() {
     int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
+    head = (head + 1) % (int64_t)ring.size();
     --count;
     return b;
   }
   void push_back(int32_t b) {
-    ring[(head + count) % num_blocks] = b;
+    ring[(head + count) % (int64_t)ring.size()] = b;
     ++count;
   }
+};
+
+struct pa_alloc {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  BlockRing free;             // device blocks, capacity num_blocks
+  std::vector<int32_t> refs;  // tables holding each block (0 = free)
+  std::vector<int32_t> copies;  // pending (source, destination) pairs, flattened
+  int32_t num_host_blocks = 0;
+  BlockRing host_free;        // host pool blocks, capacity num_host_blocks
+  int64_t num_swapped = 0;    // sequences currently on host blocks
+  struct Seq {
+    std::vector<int32_t> blocks;  // device block ids, or host block ids while swapped
+    int64_t len = 0;
+    bool swapped = false;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t pop_front() { return free.pop_front(); }
+  void push_back(int32_t b) { free.push_back(b); }
+  int64_t count() const { return free.count; }
 };
 
 extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
@@ -65,7 +90,7 @@ extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
   pa_alloc *a = new (std::nothrow) pa_alloc();
   if (!a) return pa::fail(PA_ENOMEM, "pa_alloc_create: host allocation failed");
   try {
-    a->ring.resize(num_blocks);
+    a->free.ring.resize(num_blocks);
     a->refs.assign(num_blocks, 0);
   } catch (...) {
     delete a;
@@ -84,13 +109,13 @@ extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                         i, b);
       }
       seen[b] = 1;
-      a->ring[i] = b;
+      a->free.ring[i] = b;
     }
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) a->ring[i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) a->free.ring[i] = i;
   }
-  a->head = 0;
-  a->count = num_blocks;
+  a->free.head = 0;
+  a->free.count = num_blocks;
   *out = a;
   return PA_OK;
 }
@@ -103,15 +128,17 @@ extern "C" pa_status pa_alloc_append(pa_alloc *a, int64_t seq_id, int32_t num_to
   if (!a) return pa::fail(PA_EINVAL, "pa_alloc_append: allocator is NULL");
   if (num_tokens < 0) return pa::fail(PA_EINVAL, "pa_alloc_append: num_tokens=%d", num_tokens);
   auto it = a->seqs.find(seq_id);
+  if (it != a->seqs.end() && it->second.swapped)
+    return pa::fail(PA_EINVAL, "pa_alloc_append: sequence %lld is swapped out", (long long)seq_id);
   const int64_t held = it == a->seqs.end() ? 0 : it->second.len;
   const int64_t have = it == a->seqs.end() ? 0 : (int64_t)it->second.blocks.size();
   const int64_t want = (held + num_tokens + a->block_size - 1) / a->block_size;
   // Writing into a shared last block that still has room needs a copy.
   const bool cow = num_tokens > 0 && held % a->block_size != 0 &&
                    a->refs[it->second.blocks.back()] > 1;
-  if (want - have + cow > a->count)
+  if (want - have + cow > a->count())
     return pa::fail(PA_ENOMEM, "pa_alloc_append: sequence %lld needs %lld blocks, %lld free",
-                    (long long)seq_id, (long long)(want - have + cow), (long long)a->count);
+                    (long long)seq_id, (long long)(want - have + cow), (long long)a->count());
   pa_alloc::Seq *s;
   try {
     s = &a->seqs[seq_id];
@@ -150,8 +177,13 @@ extern "C" pa_status pa_alloc_free(pa_alloc *a, int64_t seq_id) {
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end())
     return pa::fail(PA_ENOTFOUND, "pa_alloc_free: unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.blocks)
-    if (--a->refs[b] == 0) a->push_back(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.blocks) a->host_free.push_back(h);
+    --a->num_swapped;
+  } else {
+    for (int32_t b : it->second.blocks)
+      if (--a->refs[b] == 0) a->push_back(b);
+  }
   a->seqs.erase(it);
   return PA_OK;
 }
@@ -162,6 +194,9 @@ extern "C" pa_status pa_alloc_fork(pa_alloc *a, int64_t parent_id, int64_t child
   auto it = a->seqs.find(parent_id);
   if (it == a->seqs.end())
     return pa::fail(PA_ENOTFOUND, "pa_alloc_fork: unknown sequence %lld", (long long)parent_id);
+  if (it->second.swapped)
+    return pa::fail(PA_EINVAL, "pa_alloc_fork: sequence %lld is swapped out",
+                    (long long)parent_id);
   if (a->seqs.count(child_id))
     return pa::fail(PA_EINVAL, "pa_alloc_fork: sequence %lld already exists",
                     (long long)child_id);
@@ -189,7 +224,7 @@ extern "C" int32_t pa_alloc_block_refs(const pa_alloc *a, int32_t block) {
   return a->refs[block];
 }
 
-extern "C" int32_t pa_alloc_num_free(const pa_alloc *a) { return a ? (int32_t)a->count : -1; }
+extern "C" int32_t pa_alloc_num_free(const pa_alloc *a) { return a ? (int32_t)a->count() : -1; }
 
 extern "C" int32_t pa_alloc_seq_len(const pa_alloc *a, int64_t seq_id) {
   if (!a) return -1;
@@ -207,6 +242,9 @@ extern "C" pa_status pa_alloc_block_table(const pa_alloc *a, const int64_t *seq_
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return pa::fail(PA_ENOTFOUND, "pa_alloc_block_table: unknown sequence %lld",
+                      (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return pa::fail(PA_EINVAL, "pa_alloc_block_table: sequence %lld is swapped out",
                       (long long)seq_ids[i]);
     const auto &blocks = it->second.blocks;
     if ((int64_t)blocks.size() > max_blocks)
@@ -240,6 +278,9 @@ extern "C" pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const in
         return pa::fail(PA_EINVAL, "pa_alloc_step: sequence %lld listed twice",
                         (long long)seq_ids[i]);
       auto it = a->seqs.find(seq_ids[i]);
+      if (it != a->seqs.end() && it->second.swapped)
+        return pa::fail(PA_EINVAL, "pa_alloc_step: sequence %lld is swapped out",
+                        (long long)seq_ids[i]);
       const int64_t held = it == a->seqs.end() ? 0 : it->second.len;
       const int64_t have = it == a->seqs.end() ? 0 : (int64_t)it->second.blocks.size();
       const int64_t want = (held + num_tokens[i] + a->block_size - 1) / a->block_size;
@@ -260,9 +301,9 @@ extern "C" pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const in
   } catch (...) {
     return pa::fail(PA_ENOMEM, "pa_alloc_step: host allocation failed");
   }
-  if (need > a->count)
+  if (need > a->count())
     return pa::fail(PA_ENOMEM, "pa_alloc_step: the step needs %lld blocks, %lld free",
-                    (long long)need, (long long)a->count);
+                    (long long)need, (long long)a->count());
   if (total > 0 && !slots_out) return pa::fail(PA_EINVAL, "pa_alloc_step: slots_out is NULL");
   int64_t off = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -272,4 +313,124 @@ extern "C" pa_status pa_alloc_step(pa_alloc *a, const int64_t *seq_ids, const in
     off += num_tokens[i];
   }
   return pa_alloc_block_table(a, seq_ids, n, max_blocks, table_out, lens_out);
+}
+
+extern "C" pa_status pa_alloc_set_host_pool(pa_alloc *a, int32_t num_host_blocks,
+                                            const int32_t *initial_order) {
+  pa::clear_error();
+  if (!a) return pa::fail(PA_EINVAL, "pa_alloc_set_host_pool: allocator is NULL");
+  if (num_host_blocks < 0)
+    return pa::fail(PA_EINVAL, "pa_alloc_set_host_pool: num_host_blocks=%d", num_host_blocks);
+  if (a->num_swapped > 0)
+    return pa::fail(PA_EINVAL, "pa_alloc_set_host_pool: %lld sequences are swapped out",
+                    (long long)a->num_swapped);
+  BlockRing ring;
+  try {
+    ring.ring.resize(num_host_blocks);
+  } catch (...) {
+    return pa::fail(PA_ENOMEM, "pa_alloc_set_host_pool: host allocation failed");
+  }
+  if (initial_order) {
+    std::vector<char> seen;
+    try {
+      seen.assign(num_host_blocks, 0);
+    } catch (...) {
+      return pa::fail(PA_ENOMEM, "pa_alloc_set_host_pool: host allocation failed");
+    }
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t b = initial_order[i];
+      if (b < 0 || b >= num_host_blocks || seen[b])
+        return pa::fail(PA_EINVAL,
+                        "pa_alloc_set_host_pool: initial_order is not a permutation "
+                        "(entry %d = %d)", i, b);
+      seen[b] = 1;
+      ring.ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_host_blocks; ++i) ring.ring[i] = i;
+  }
+  ring.count = num_host_blocks;
+  a->host_free = std::move(ring);
+  a->num_host_blocks = num_host_blocks;
+  return PA_OK;
+}
+
+extern "C" int32_t pa_alloc_num_free_host(const pa_alloc *a) {
+  return a ? (int32_t)a->host_free.count : -1;
+}
+
+extern "C" int32_t pa_alloc_is_swapped(const pa_alloc *a, int64_t seq_id) {
+  if (!a) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+// Shared checks of the two swap directions: the sequence exists and is on
+// the expected side, and pairs_out has room for one pair per block.
+static pa_status swap_lookup(pa_alloc *a, const char *fn, int64_t seq_id, bool want_swapped,
+                             int32_t max_pairs, int32_t *pairs_out, int32_t *num_pairs,
+                             pa_alloc::Seq **seq) {
+  if (!a || !num_pairs || max_pairs < 0 || (max_pairs > 0 && !pairs_out))
+    return pa::fail(PA_EINVAL, "%s: bad arguments", fn);
+  *num_pairs = 0;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end())
+    return pa::fail(PA_ENOTFOUND, "%s: unknown sequence %lld", fn, (long long)seq_id);
+  if (it->second.swapped != want_swapped)
+    return pa::fail(PA_EINVAL, "%s: sequence %lld is %s", fn, (long long)seq_id,
+                    want_swapped ? "not swapped out" : "already swapped out");
+  if ((int64_t)it->second.blocks.size() > max_pairs)
+    return pa::fail(PA_EINVAL, "%s: sequence %lld holds %zu blocks > max_pairs %d", fn,
+                    (long long)seq_id, it->second.blocks.size(), max_pairs);
+  *seq = &it->second;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_alloc_swap_out(pa_alloc *a, int64_t seq_id, int32_t max_pairs,
+                                       int32_t *pairs_out, int32_t *num_pairs) {
+  pa::clear_error();
+  const char *fn = "pa_alloc_swap_out";
+  pa_alloc::Seq *s = nullptr;
+  pa_status st = swap_lookup(a, fn, seq_id, false, max_pairs, pairs_out, num_pairs, &s);
+  if (st != PA_OK) return st;
+  const int64_t n = (int64_t)s->blocks.size();
+  if (n > a->host_free.count)
+    return pa::fail(PA_ENOMEM, "%s: sequence %lld needs %lld host blocks, %lld free", fn,
+                    (long long)seq_id, (long long)n, (long long)a->host_free.count);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t dev = s->blocks[i], host = a->host_free.pop_front();
+    pairs_out[2 * i] = dev;
+    pairs_out[2 * i + 1] = host;
+    s->blocks[i] = host;
+    if (--a->refs[dev] == 0) a->push_back(dev);
+  }
+  s->swapped = true;
+  ++a->num_swapped;
+  *num_pairs = (int32_t)n;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_alloc_swap_in(pa_alloc *a, int64_t seq_id, int32_t max_pairs,
+                                      int32_t *pairs_out, int32_t *num_pairs) {
+  pa::clear_error();
+  const char *fn = "pa_alloc_swap_in";
+  pa_alloc::Seq *s = nullptr;
+  pa_status st = swap_lookup(a, fn, seq_id, true, max_pairs, pairs_out, num_pairs, &s);
+  if (st != PA_OK) return st;
+  const int64_t n = (int64_t)s->blocks.size();
+  if (n > a->count())
+    return pa::fail(PA_ENOMEM, "%s: sequence %lld needs %lld blocks, %lld free", fn,
+                    (long long)seq_id, (long long)n, (long long)a->count());
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t host = s->blocks[i], dev = a->pop_front();
+    pairs_out[2 * i] = host;
+    pairs_out[2 * i + 1] = dev;
+    s->blocks[i] = dev;
+    a->refs[dev] = 1;
+    a->host_free.push_back(host);
+  }
+  s->swapped = false;
+  --a->num_swapped;
+  *num_pairs = (int32_t)n;
+  return PA_OK;
 }

@@ -1,14 +1,19 @@
-// Whole-block copies inside the two pools, for copy-on-write sharing
-// ("vLLM Architecture, Memory and Benchmarks Deep Dive", section 2,
-// "Copy-on-Write (CoW) Branching": a shared block is cloned when the
-// sequences holding it diverge).
+// Whole-block copies, for copy-on-write sharing inside the two pools ("vLLM
+// Architecture, Memory and Benchmarks Deep Dive", section 2, "Copy-on-Write
+// (CoW) Branching": a shared block is cloned when the sequences holding it
+// diverge) and for swapping blocks between device pools and pools in pinned
+// host memory ("Inside vLLM: Anatomy of a High-Throughput LLM Inference
+// System", "Memory-Efficient KV Cache Storage": blocks are paged out to host
+// memory and back).
 //
 // A block is contiguous in each pool ([num_kv_heads][block_size][head_dim]),
 // so a copy is a straight memcpy of block_bytes. Grid: x = 16 KiB slices of
 // a block, y = pairs. Each thread issues all of its K and V loads of a slice
-// before the stores, so a workgroup keeps 32 KiB in flight. The pair is read
-// once per workgroup (the same address in every lane); pairs with an id
-// outside the pool, or with source equal to destination, do nothing.
+// before the stores, so a workgroup keeps 32 KiB in flight (for a host-side
+// pool these are PCIe reads or writes; many workgroups in flight hide their
+// latency). The pair is read once per workgroup (the same address in every
+// lane); pairs with an id outside its pool do nothing, and so do pairs with
+// source equal to destination when both sides are the same pools.
 #include "launch.h"
 #include "pa_device.h"
 
@@ -34,20 +39,25 @@ struct CopyUnit<2> {
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
+// Source and destination pools may be the same buffers (copy-on-write):
+// destinations are never sources, so no byte is both read and written and the
+// restrict qualifiers still hold.
 template <int UNIT>
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    uint8_t *__restrict__ key_cache, uint8_t *__restrict__ value_cache,
-    const int32_t *__restrict__ pairs, int32_t num_pairs, int32_t num_blocks,
-    int64_t block_bytes) {
+    const uint8_t *__restrict__ src_key, const uint8_t *__restrict__ src_value,
+    uint8_t *__restrict__ dst_key, uint8_t *__restrict__ dst_value,
+    const int32_t *__restrict__ pairs, int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks,
+    int64_t block_bytes, int32_t skip_same) {
   using T = typename CopyUnit<UNIT>::T;
   const int64_t units = block_bytes / UNIT;
   for (int32_t pr = blockIdx.y; pr < num_pairs; pr += gridDim.y) {
     const int32_t src = pairs[2 * pr], dst = pairs[2 * pr + 1];
-    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) continue;
-    const T *ks = reinterpret_cast<const T *>(key_cache + (int64_t)src * block_bytes);
-    const T *vs = reinterpret_cast<const T *>(value_cache + (int64_t)src * block_bytes);
-    T *kd = reinterpret_cast<T *>(key_cache + (int64_t)dst * block_bytes);
-    T *vd = reinterpret_cast<T *>(value_cache + (int64_t)dst * block_bytes);
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+    if (skip_same && src == dst) continue;
+    const T *ks = reinterpret_cast<const T *>(src_key + (int64_t)src * block_bytes);
+    const T *vs = reinterpret_cast<const T *>(src_value + (int64_t)src * block_bytes);
+    T *kd = reinterpret_cast<T *>(dst_key + (int64_t)dst * block_bytes);
+    T *vd = reinterpret_cast<T *>(dst_value + (int64_t)dst * block_bytes);
     for (int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll; base < units;
          base += (int64_t)gridDim.x * kCopyThreads * kCopyUnroll) {
       T k[kCopyUnroll], v[kCopyUnroll];
@@ -71,27 +81,38 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
-pa_status launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs,
-                             int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
-                             hipStream_t stream) {
+pa_status launch_move_blocks(const void *src_key, const void *src_value, void *dst_key,
+                             void *dst_value, const int32_t *pairs, int32_t num_pairs,
+                             int64_t block_bytes, int32_t src_blocks, int32_t dst_blocks,
+                             bool skip_same, const char *fn, hipStream_t stream) {
   const int unit = (block_bytes % 16 == 0) ? 16 : (block_bytes % 4 == 0) ? 4 : 2;
   const int64_t units = block_bytes / unit;
   int64_t gx = (units + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
   if (gx > 1024) gx = 1024;  // the slice loop covers the rest
   const unsigned gy = (unsigned)(num_pairs < 65535 ? num_pairs : 65535);
   const dim3 grid((unsigned)gx, gy);
-  auto kc = (uint8_t *)key_cache;
-  auto vc = (uint8_t *)value_cache;
+  auto sk = (const uint8_t *)src_key;
+  auto sv = (const uint8_t *)src_value;
+  auto dk = (uint8_t *)dst_key;
+  auto dv = (uint8_t *)dst_value;
+  const int32_t same = skip_same ? 1 : 0;
   if (unit == 16)
-    copy_blocks_kernel<16><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
-                                                              num_blocks, block_bytes);
+    copy_blocks_kernel<16><<<grid, kCopyThreads, 0, stream>>>(
+        sk, sv, dk, dv, pairs, num_pairs, src_blocks, dst_blocks, block_bytes, same);
   else if (unit == 4)
-    copy_blocks_kernel<4><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
-                                                             num_blocks, block_bytes);
+    copy_blocks_kernel<4><<<grid, kCopyThreads, 0, stream>>>(
+        sk, sv, dk, dv, pairs, num_pairs, src_blocks, dst_blocks, block_bytes, same);
   else
-    copy_blocks_kernel<2><<<grid, kCopyThreads, 0, stream>>>(kc, vc, pairs, num_pairs,
-                                                             num_blocks, block_bytes);
-  return check_launch("pa_copy_blocks");
+    copy_blocks_kernel<2><<<grid, kCopyThreads, 0, stream>>>(
+        sk, sv, dk, dv, pairs, num_pairs, src_blocks, dst_blocks, block_bytes, same);
+  return check_launch(fn);
+}
+
+pa_status launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs,
+                             int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                             hipStream_t stream) {
+  return launch_move_blocks(key_cache, value_cache, key_cache, value_cache, pairs, num_pairs,
+                            block_bytes, num_blocks, num_blocks, true, "pa_copy_blocks", stream);
 }
 
 }  // namespace pa

@@ -11,6 +11,13 @@ pa_status launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);
 
+// Block copies from one pair of pools to another (device memory or pinned,
+// device-mapped host memory); pairs are (source, destination) block ids.
+pa_status launch_move_blocks(const void *src_key, const void *src_value, void *dst_key,
+                             void *dst_value, const int32_t *pairs, int32_t num_pairs,
+                             int64_t block_bytes, int32_t src_blocks, int32_t dst_blocks,
+                             bool skip_same, const char *fn, hipStream_t stream);
+
 pa_status launch_cache_write(const void *key, const void *value, void *key_cache,
                              void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -114,6 +114,74 @@ extern "C" pa_status pa_copy_blocks(void *key_cache, void *value_cache, const in
                                 num_blocks, stream);
 }
 
+// True when the bytes [ptr, ptr + bytes) start and end in memory a kernel on
+// the current device may address at these same pointers: device memory of
+// this device, or pinned host memory mapped into the device's address space.
+// Anything else (pageable host memory, another device's memory) is refused
+// before a launch could fault on it.
+static pa_status check_reachable(const char *fn, const char *what, const void *ptr,
+                                 int64_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return pa::fail(PA_EHIP, "%s: hipGetDevice failed", fn);
+  }
+  for (int end = 0; end < 2; ++end) {
+    const char *p = (const char *)ptr + (end ? bytes - 1 : 0);
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+      (void)hipGetLastError();
+      return pa::fail(PA_EINVAL, "%s: %s is neither device memory nor pinned host memory", fn,
+                      what);
+    }
+    const bool on_device = attr.type == hipMemoryTypeDevice && attr.device == dev;
+    const bool pinned_host = attr.type == hipMemoryTypeHost && attr.devicePointer == (void *)p;
+    if (!on_device && !pinned_host)
+      return pa::fail(PA_EINVAL,
+                      "%s: %s (%s byte) is not device memory of device %d nor pinned host "
+                      "memory mapped at the same address", fn, what, end ? "last" : "first",
+                      dev);
+  }
+  return PA_OK;
+}
+
+extern "C" pa_status pa_swap_blocks(const void *src_key_cache, const void *src_value_cache,
+                                    int32_t src_num_blocks, void *dst_key_cache,
+                                    void *dst_value_cache, int32_t dst_num_blocks,
+                                    const int32_t *block_pairs, int32_t num_pairs,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    pa_dtype kv_dtype, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_swap_blocks";
+  if (num_pairs < 0) return pa::fail(PA_EINVAL, "%s: num_pairs=%d < 0", fn, num_pairs);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || src_num_blocks <= 0 ||
+      dst_num_blocks <= 0)
+    return pa::fail(PA_EINVAL,
+                    "%s: num_kv_heads=%d head_dim=%d block_size=%d src_num_blocks=%d "
+                    "dst_num_blocks=%d", fn, num_kv_heads, head_dim, block_size, src_num_blocks,
+                    dst_num_blocks);
+  if (!dtype_ok(kv_dtype) && kv_dtype != PA_FP8_E4M3)
+    return pa::fail(PA_EINVAL, "%s: bad kv_dtype %d", fn, (int)kv_dtype);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_pairs)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  const int64_t block_bytes =
+      (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
+  const struct { const char *what; const void *p; int64_t bytes; } spans[] = {
+      {"src_key_cache", src_key_cache, block_bytes * src_num_blocks},
+      {"src_value_cache", src_value_cache, block_bytes * src_num_blocks},
+      {"dst_key_cache", dst_key_cache, block_bytes * dst_num_blocks},
+      {"dst_value_cache", dst_value_cache, block_bytes * dst_num_blocks},
+      {"block_pairs", block_pairs, (int64_t)num_pairs * 2 * (int64_t)sizeof(int32_t)}};
+  for (const auto &sp : spans) {
+    const pa_status st = check_reachable(fn, sp.what, sp.p, sp.bytes);
+    if (st != PA_OK) return st;
+  }
+  return pa::launch_move_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                                block_pairs, num_pairs, block_bytes, src_num_blocks,
+                                dst_num_blocks, src_key_cache == dst_key_cache, fn, stream);
+}
+
 extern "C" pa_status pa_decode(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

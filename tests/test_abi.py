@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
     for n in ["pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned", "pa_reduce",
               "pa_prefill_chunk", "pa_alloc_create", "pa_alloc_append", "pa_alloc_free",
               "pa_alloc_block_table", "pa_last_error", "pa_reshape_and_cache_fp8",
-              "pa_decode_fp8", "pa_decode_partitioned_fp8"]:
+              "pa_decode_fp8", "pa_decode_partitioned_fp8", "pa_swap_blocks",
+              "pa_alloc_swap_out", "pa_alloc_swap_in", "pa_alloc_set_host_pool"]:
         assert n in names
 
 
@@ -151,3 +152,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libpa.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.lib()
+
+
+def test_swap_blocks_rejects_bad_arguments():
+    lib = _lib.lib()
+
+    def sw(n=4, hkv=4, d=256, bs=16, snb=10, dnb=10, dt=1):
+        return lib.pa_swap_blocks(NULL, NULL, snb, NULL, NULL, dnb, NULL, n, hkv, d, bs, dt, NULL)
+    assert sw(n=-1) == _lib.PA_EINVAL and b"num_pairs" in lib.pa_last_error()
+    assert sw(snb=0) == _lib.PA_EINVAL
+    assert sw(dnb=-3) == _lib.PA_EINVAL
+    assert sw(bs=0) == _lib.PA_EINVAL
+    assert sw(dt=7) == _lib.PA_EINVAL
+    assert sw() == _lib.PA_EINVAL and b"null" in lib.pa_last_error()
+    assert sw(n=0) == _lib.PA_OK                                    # no pairs: no-op
+    assert sw(n=0, dt=_lib.PA_FP8_E4M3) == _lib.PA_OK

@@ -229,3 +229,129 @@ def test_step_errors():
     with pytest.raises(PAError) as e:
         a.step([1, 2, 3], [8, 4, 8], 4)                          # needs 2+1+2 blocks, 4 free
     assert e.value.status == PA_ENOMEM and a.num_free() == 4 and a.seq_len(1) == 7
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_swap_matches_oracle_model(seed):
+    """Appends, forks, releases, swap-outs and swap-ins in random order: the
+    native allocator and the oracle's model give the same slots, swap pairs,
+    tables, device and host free counts and holder counts at every step, and
+    refuse the same operations."""
+    rng = random.Random(300 + seed)
+    nb, bs, nh = rng.choice([(24, 4, 16), (64, 16, 40), (40, 1, 50), (30, 5, 10)])
+    order, horder = list(range(nb)), list(range(nh))
+    rng.shuffle(order)
+    rng.shuffle(horder)
+    a = BlockAllocator(nb, bs, initial_order=order)
+    a.set_host_pool(nh, initial_order=horder)
+    m = model.BlockAllocatorModel(nb, bs, initial_order=order, num_host_blocks=nh,
+                                  host_initial_order=horder)
+    live, out = set(), set()
+    for _ in range(500):
+        op = rng.random()
+        if op < 0.4 or not (live | out):
+            sid = rng.choice(sorted(live)) if live and rng.random() < 0.8 else rng.randrange(50)
+            n = rng.randint(0, 2 * bs + 1)
+            if sid in out:
+                with pytest.raises(PAError) as e:
+                    a.append(sid, n)
+                assert e.value.status == PA_EINVAL
+                continue
+            try:
+                want = m.append(sid, n)
+            except model.OutOfBlocks:
+                with pytest.raises(PAError) as e:
+                    a.append(sid, n)
+                assert e.value.status == PA_ENOMEM
+                continue
+            assert list(a.append(sid, n)) == want
+            live.add(sid)
+        elif op < 0.5 and live:
+            parent = rng.choice(sorted(live))
+            child = rng.randrange(50, 100)
+            if child in live or child in out:
+                continue
+            m.fork(parent, child)
+            a.fork(parent, child)
+            live.add(child)
+        elif op < 0.7 and live:
+            sid = rng.choice(sorted(live))
+            try:
+                want = m.swap_out(sid)
+            except model.OutOfBlocks:
+                with pytest.raises(PAError) as e:
+                    a.swap_out(sid)
+                assert e.value.status == PA_ENOMEM
+                continue
+            assert [tuple(p) for p in a.swap_out(sid).tolist()] == want
+            live.discard(sid)
+            out.add(sid)
+        elif op < 0.85 and out:
+            sid = rng.choice(sorted(out))
+            try:
+                want = m.swap_in(sid)
+            except model.OutOfBlocks:
+                with pytest.raises(PAError) as e:
+                    a.swap_in(sid)
+                assert e.value.status == PA_ENOMEM
+                continue
+            assert [tuple(p) for p in a.swap_in(sid).tolist()] == want
+            out.discard(sid)
+            live.add(sid)
+        else:
+            sid = rng.choice(sorted(live | out))
+            m.free(sid)
+            a.free(sid)
+            live.discard(sid)
+            out.discard(sid)
+        assert [tuple(p) for p in a.take_copies().tolist()] == m.take_copies()
+        assert a.num_free() == m.num_free() and a.num_free_host() == m.num_free_host()
+        assert [a.block_refs(b) for b in range(nb)] == [m.refs.get(b, 0) for b in range(nb)]
+        for s in live | out:
+            assert a.is_swapped(s) == (1 if s in out else 0)
+            assert a.seq_len(s) == m.lengths[s]
+        if live:
+            ids = sorted(live)
+            maxb = max(len(m.tables[s]) for s in ids) + 1
+            t_m, l_m = m.block_table(ids, maxb)
+            t_a, l_a = a.block_table(ids, maxb)
+            assert np.array_equal(t_a, np.array(t_m, dtype=np.int32))
+            assert list(l_a) == l_m
+
+
+def test_swap_errors():
+    a = BlockAllocator(8, 4)
+    a.append(1, 6)                                              # blocks 0, 1
+    with pytest.raises(PAError) as e:
+        a.swap_out(1)                                           # no host pool yet
+    assert e.value.status == PA_ENOMEM
+    a.set_host_pool(3)
+    with pytest.raises(PAError) as e:
+        a.swap_out(7)
+    assert e.value.status == PA_ENOTFOUND
+    with pytest.raises(PAError) as e:
+        a.swap_in(1)                                            # not swapped out
+    assert e.value.status == PA_EINVAL
+    assert a.swap_out(1).tolist() == [[0, 0], [1, 1]]
+    assert a.is_swapped(1) == 1 and a.num_free() == 8 and a.num_free_host() == 1
+    for bad in (lambda: a.append(1, 1), lambda: a.fork(1, 2), lambda: a.block_table([1], 4),
+                lambda: a.step([1], [1], 4), lambda: a.swap_out(1), lambda: a.set_host_pool(5)):
+        with pytest.raises(PAError) as e:
+            bad()
+        assert e.value.status == PA_EINVAL
+    with pytest.raises(PAError) as e:
+        a.set_host_pool(4, initial_order=[0, 1, 1, 2])
+    assert e.value.status == PA_EINVAL
+    a.append(2, 32)                                             # takes all 8 device blocks
+    with pytest.raises(PAError) as e:
+        a.swap_in(1)
+    assert e.value.status == PA_ENOMEM
+    assert a.is_swapped(1) == 1 and a.num_free_host() == 1      # unchanged
+    a.free(2)
+    assert a.swap_in(1).tolist() == [[0, 2], [1, 3]]            # device queue after block 1
+    assert a.num_free_host() == 3 and a.seq_len(1) == 6
+    a.swap_out(1)
+    a.free(1)                                                   # host blocks back
+    assert a.num_free_host() == 3 and a.is_swapped(1) == -1
+    a.set_host_pool(0)
+    assert a.num_free_host() == 0
