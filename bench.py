@@ -7,7 +7,7 @@ the needed size - run as 16 independent layers back to back.
 
 One step = for each of the 16 layers: the slot-mapped write of the step's
 new K/V (pa_reshape_and_cache), split-context decode (pa_decode_partitioned,
-1024-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
+2048-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
 slot mappings come from the host allocator's layout before timing starts;
 every input is resident in HBM when the timed region begins.
 
@@ -47,9 +47,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix cores, vendor figure
 HERE = os.path.dirname(os.path.abspath(__file__))
 # HBM bytes per decode launch, measured with FETCH_SIZE / WRITE_SIZE counters
 # and scaled by the same counters' reading for a plain copy of known size.
-TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_persistent_mixed_64seq_hbm_counters.md")
+TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_mfma_mixed_64seq_hbm_counters.md")
 TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
-                   for f in ("decode_persistent.hip", "pa_device.h", "persistent_plan.h")]
+                   for f in ("decode_mfma.hip", "pa_device.h", "persistent_plan.h")]
 FP8_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_fp8_mixed_64seq_16layer.md")
 FP8_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
                        for f in ("decode_fp8.hip", "pa_device.h", "persistent_plan.h")]
@@ -58,8 +58,11 @@ PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", 
                            for f in ("prefill_mfma.hip", "pa_device.h")]
 # Partition size per workload: the long-context configuration fixes 512
 # tokens; for the others it is the fastest measured on MI355X (mixed
-# 16-layer step: 1.450 ms at 512, 1.376 ms at 1024, 1.373 ms at 2048).
-DEFAULT_PARTITION = {"mixed": 1024, "long": 512, "uniform": 256}
+# 16-layer step with the matrix-core decode: 1.406 ms at 512, 1.348 ms at
+# 1024, 1.311 ms at 2048, 1.822 ms at 4096, where too few units are left to
+# balance the CUs). The FP8 leg keeps 1024, its measured best.
+DEFAULT_PARTITION = {"mixed": 2048, "long": 512, "uniform": 256}
+FP8_DEFAULT_PARTITION = {"mixed": 1024, "long": 512, "uniform": 256}
 WORKLOAD_NAMES = {
     "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
     "long": "long-context split decode, 4 seqs {8192, 16384, 32768, 32768}, bs 32",
@@ -74,7 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="split-context partition in tokens (default: 1024 for the mixed "
+                    help="split-context partition in tokens (default: 2048 for the mixed "
                          "workload, 512 for the long one as its configuration states, 256 "
                          "for the uniform one)")
     ap.add_argument("--workload", default="mixed", choices=["mixed", "long", "uniform"],
@@ -88,7 +91,8 @@ def parse():
     ap.add_argument("--fp8", type=int, default=1,
                     help="also time the step over FP8 (E4M3FN) pools (0: skip)")
     ap.add_argument("--fp8-partition-size", type=int, default=None,
-                    help="partition size of the FP8 leg (default: the BF16 one)")
+                    help="partition size of the FP8 leg (default: 1024 for the mixed workload, "
+                         "512 for the long one, 256 for the uniform one)")
     ap.add_argument("--loop-steps", type=int, default=50,
                     help="timed iterations of the continuous-batching loop leg (0 skips it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
@@ -588,7 +592,7 @@ def main():
     }
     if args.fp8:
         del po, pm, ps, outs
-        result["fp8"] = fp8_leg(layers, meta, args.fp8_partition_size or P, args.steps,
+        result["fp8"] = fp8_leg(layers, meta, args.fp8_partition_size or FP8_DEFAULT_PARTITION[W], args.steps,
                                 args.warmup, dev, W, args.seed)
     if args.prefill_reps > 0:
         del layers

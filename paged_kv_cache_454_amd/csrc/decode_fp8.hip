@@ -13,7 +13,7 @@
 // padded query heads x 256 channels x 32 tokens), which v_mfma_f32_16x16x32
 // _bf16 does in 32 instructions.
 //
-// Work decomposition and streaming are those of the BF16 persistent kernel:
+// Work decomposition and streaming are those of the BF16 matrix-core kernel:
 // one 8-wave workgroup per compute unit owns up to 64 units (planned on the
 // device from the context lengths), each wave streams its tiles of all of
 // them through a two-deep register ring, and the 8 waves' partial softmax

@@ -66,10 +66,9 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream);
 // rows only). Returns false when the shape is not covered.
 bool launch_decode_tiled(const DecodeParams &p, unsigned grid, hipStream_t stream);
 
-// Persistent variant of the same shape class (single pass or partitioned):
-// one 8-wave workgroup per compute unit streaming a list of units. Returns
-// false when the shape is not covered.
-bool launch_decode_persistent(const DecodeParams &p, hipStream_t stream);
+// Matrix-core decode for BF16, head_dim 256, block_size % 16 == 0 (decode
+// rows only). Returns false when the shape is not covered.
+bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 
 // Matrix-core decode over FP8 pools (head_dim 256, block_size % 16 == 0,
 // partitions of a multiple of 32 tokens). Returns false when the shape is
