@@ -21,7 +21,7 @@
 // Per tile (16 tokens of one KV head inside one block: 8 KiB of K and 8 KiB
 // of V):
 //  * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16 (M = 16 tokens, N = 16
-//    query heads, the group's heads padded with zero queries, K = 256
+//    columns, the group's G query heads and repeats of them, K = 256
 //    channels in 8 steps). Lane (m, g) (m = lane % 16, g = lane / 16) needs
 //    16-byte pieces of token row m. Eight wavefront loads each read whole
 //    128-byte lines of 8 rows (lane (m, g): row m % 8 + 8 (i & 1), byte
@@ -314,8 +314,11 @@ void decode_mfma_kernel(DecodeParams p) {
   const float sl2 = p.scale * kLog2e;
   f32x4 o[16];
   float m_run, l_run;
+  // Columns n >= G repeat query head n % G: MFMA columns do not mix, those
+  // columns are never stored, and their maxima equal a real head's, so they
+  // trigger no extra rescales.
   const bool live_head = n16 < G;
-  const int qh = live_head ? n16 : 0;
+  const int qh = n16 % G;
 
   // S^T, softmax and the weights (B operand of P.V) for one tile.
   auto qk_softmax = [&](const u32x4(&kraw)[KL], int qslot, int nvalid) -> u32x2 {
@@ -340,14 +343,14 @@ void decode_mfma_kernel(DecodeParams p) {
       const uint4 q0 = qs[qslot][qh][8 * pp + grp];
       const uint4 q1 = qs[qslot][qh][8 * pp + 4 + grp];
       u32x4 b0, b1;
-      b0[0] = live_head ? q0.x : 0u;
-      b0[1] = live_head ? q0.y : 0u;
-      b0[2] = live_head ? q0.z : 0u;
-      b0[3] = live_head ? q0.w : 0u;
-      b1[0] = live_head ? q1.x : 0u;
-      b1[1] = live_head ? q1.y : 0u;
-      b1[2] = live_head ? q1.z : 0u;
-      b1[3] = live_head ? q1.w : 0u;
+      b0[0] = q0.x;
+      b0[1] = q0.y;
+      b0[2] = q0.z;
+      b0[3] = q0.w;
+      b1[0] = q1.x;
+      b1[1] = q1.y;
+      b1[2] = q1.z;
+      b1[3] = q1.w;
       s0 = mfma32(k0, b0, s0);
       s1 = mfma32(k1, b1, s1);
     }
