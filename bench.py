@@ -168,6 +168,25 @@ def timed_launches(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
+def decode_launch_ms(launch, nlayers, reps, stream):
+    """Mean duration (ms) of one decode launch: each repetition runs the
+    decode of every layer back to back between two HIP events on the stream
+    the kernels are launched on. The host enqueues a launch much faster than
+    the GPU runs it, so the queue stays ahead and the events see the
+    kernels (and the gaps between them), not the host's submission time."""
+    import torch
+    pairs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for li in range(nlayers):
+            launch(li)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / nlayers
+
+
 def prefill_leg(seed, reps, dev):
     """Chunked prefill at full size: the chunk's slot write and the causal
     paged attention of its 8,192 query rows."""
@@ -437,36 +456,30 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     bt, cl, sm = meta["block_tables"], meta["context_lens"], meta["slot_mapping"]
     scale = meta["scale"]
     stream = torch.cuda.current_stream()
-    ev = []
 
-    def step(record):
+    def decode(li):
+        kc, vc = pools[li]
+        pa.pa_decode_partitioned_fp8(po, pm, ps, layers[li]["query"], kc, vc, bt, cl, scale, ks,
+                                     vs, P, stream=stream)
+
+    def step():
         for li, L in enumerate(layers):
             kc, vc = pools[li]
             pa.pa_reshape_and_cache_fp8(L["key"], L["value"], kc, vc, sm, ks, vs, stream=stream)
-            if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            pa.pa_decode_partitioned_fp8(po, pm, ps, L["query"], kc, vc, bt, cl, scale, ks, vs, P,
-                                         stream=stream)
-            if record:
-                e1.record(stream)
-                ev.append((e0, e1))
+            decode(li)
             pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
 
     for _ in range(warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(steps):
-        step(False)
+        step()
     b.record(stream)
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / steps
-    for _ in range(max(3, min(steps, 20))):
-        step(True)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    kern_ms = decode_launch_ms(decode, len(layers), max(3, min(steps, 20)), stream)
     kv_bytes_layer = int(lens.sum()) * hkv * d * 2      # one byte per element, K and V
     k_gbs = kv_bytes_layer / (kern_ms * 1e-3) / 1e9
     del pools, po, pm, ps, outs
@@ -517,42 +530,34 @@ def main():
     bt, cl, sm = meta["block_tables"], meta["context_lens"], meta["slot_mapping"]
     scale = meta["scale"]
     stream = torch.cuda.current_stream()
-    ev = []
 
-    def step(record):
+    def decode(li):
+        L = layers[li]
+        pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
+                                 bt, cl, scale, P, stream=stream)
+
+    def step():
         for li, L in enumerate(layers):
             pa.pa_reshape_and_cache(L["key"], L["value"], L["key_cache"], L["value_cache"], sm,
                                     stream=stream)
-            if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
-                                     bt, cl, scale, P, stream=stream)
-            if record:
-                e1.record(stream)
-                ev.append((e0, e1))
+            decode(li)
             pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for _ in range(args.steps):
-        step(False)
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # Decode-kernel launches timed on their own stream (a separate pass so the
-    # step timing above carries no event overhead).
-    torch.cuda.synchronize()
-    for _ in range(max(3, min(args.steps, 20))):
-        step(True)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b in ev]
-    kern_ms = float(np.mean(durs))
+    # The decode kernel's own launches, timed in a separate pass (so the step
+    # timing above carries no event overhead) on the stream they run on.
+    kern_ms = decode_launch_ms(decode, len(layers), max(3, min(args.steps, 20)), stream)
 
     hkv = inputs.PRESETS[W]["num_kv_heads"]
     kv_bytes_layer = int(lens.sum()) * hkv * d * 2 * 2
