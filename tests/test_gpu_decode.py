@@ -224,3 +224,26 @@ def test_lse_merge_with_far_apart_partition_maxima():
     spread = np.nanmax(pm[0, 0]) - np.nanmin(pm[0, 0, :16])
     assert spread > 20
     assert G.max_err(G.host(got), want) <= G.BF16_TOL
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 7, 8])
+def test_matrix_core_groups(group):
+    """Every group size the matrix-core kernel instantiates (query heads per
+    KV head 1..8; its MFMA columns beyond the group repeat real heads), in
+    single-pass and partitioned mode. The partitioned call has more units than
+    CUs (24 sequences x 2 KV heads x 8 partitions of 256 tokens), so it takes
+    the persistent path too; contexts span several tiles with ragged tails,
+    block size 16 and 32."""
+    print(f"[decode] matrix-core group={group}", flush=True)
+    rng = np.random.default_rng(40 + group)
+    for bs in (16, 32):
+        lens = [int(x) for x in rng.integers(1, 2048, size=24)]
+        lens[0], lens[1] = 2048, 16
+        case = inputs.decode_case(lens, 2 * group, 2, 256, bs, dtype="bf16", pool_factor=1.2,
+                                  seed=group * 10 + bs)
+        t = G.to_dev(case)
+        G.write(t)
+        want = _oracle_decode(case)
+        assert G.max_err(G.host(G.decode(t, case)), want) <= G.BF16_TOL, (group, bs)
+        got_p, *_ = G.partitioned(t, case, 256)
+        assert G.max_err(G.host(got_p), want) <= G.BF16_TOL, (group, bs)
