@@ -32,7 +32,7 @@
 //    zeros. Each 16-byte piece feeds two MFMA steps of 8 channels; the query
 //    fragment of a step (B operand, lane (head n, g)) takes the same
 //    channels 64j + 16g + 8h .. +7, so the contraction pairs every channel
-//    once. Query heads beyond the group are zero columns.
+//    once. Columns beyond the group repeat real heads and are never stored.
 //  * The accumulator gives lane (n, g) the logits of head n for tokens
 //    4g .. 4g+3 of each half: softmax is per-lane work plus two lane swaps
 //    (v_permlane16_swap, v_permlane32_swap) for the max and the sum. Online
@@ -357,8 +357,11 @@ void decode_fp8_kernel(DecodeParams p) {
   const float vsc = p.v_scale;
   f32x4 o[16];
   float m_run, l_run;
+  // Columns n >= G repeat query head n % G: MFMA columns do not mix, those
+  // columns are never stored, and their maxima equal a real head's, so they
+  // trigger no extra rescales.
   const bool live_head = n16 < G;
-  const int qh = live_head ? n16 : 0;
+  const int qh = n16 % G;
 
   // S^T, softmax and the weights (B operand of P.V) for one tile.
   auto qk_softmax = [&](const u32x4(&kraw)[KL], int qslot, int nvalid) -> u32x4 {
@@ -386,10 +389,10 @@ void decode_fp8_kernel(DecodeParams p) {
       for (int h = 0; h < 2; ++h) {
         const uint4 q4 = qs[qslot][qh][8 * j + 2 * grp + h];
         u32x4 qb;
-        qb[0] = live_head ? q4.x : 0u;
-        qb[1] = live_head ? q4.y : 0u;
-        qb[2] = live_head ? q4.z : 0u;
-        qb[3] = live_head ? q4.w : 0u;
+        qb[0] = q4.x;
+        qb[1] = q4.y;
+        qb[2] = q4.z;
+        qb[3] = q4.w;
         s0 = mfma(widen8(kt[j][2 * h], kt[j][2 * h + 1]), qb, s0);
         s1 = mfma(widen8(kt[4 + j][2 * h], kt[4 + j][2 * h + 1]), qb, s1);
       }
