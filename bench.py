@@ -355,6 +355,43 @@ def swap_leg(seed, reps, dev):
     return res
 
 
+def read_ceiling(dev, seed, reps=5):
+    """Measured HBM read ceilings to set beside the 8 TB/s vendor peak: the
+    library's read probe (pa_read_probe: 8 KiB blocks, decode's non-temporal
+    16-byte loads) over a 4 GiB pool, once in address order (a streaming
+    read) and once in a seeded random block order (decode's gather pattern
+    without its arithmetic). Best of `reps`, HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_454_amd as pa
+    pool = torch.ones(1 << 30, dtype=torch.int32, device=dev)   # 4 GiB
+    nblocks = pool.numel() * 4 // 8192
+    sink = torch.empty(int(pa.binding.lib().pa_read_probe_sink_words()), dtype=torch.int32,
+                       device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"kernel": "pa_read_probe", "pool_bytes": pool.numel() * 4, "unit": "GB/s"}
+    orders = {"sequential": torch.arange(nblocks, dtype=torch.int32, device=dev),
+              "random_8k_blocks": torch.from_numpy(
+                  np.random.default_rng(seed + 3).permutation(nblocks).astype(np.int32)).to(dev)}
+    for name, order in orders.items():
+        pa.pa_read_probe(pool, order, sink, stream=stream)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            pa.pa_read_probe(pool, order, sink, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        gbs = nblocks * 8192 / (best * 1e-3) / 1e9
+        res[name] = {"value": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del pool, orders, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def loop_leg(seed, steps, dev):
     """Continuous-batching decode loop (``DecodeLoop``): 64 batch slots, 16
     layers of the mixed workload's shape (24/4 heads, d 256, block 16,
@@ -607,6 +644,7 @@ def main():
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)
         result["swap"] = swap_leg(args.seed, args.prefill_reps, dev)
+        result["hbm_read_ceiling"] = read_ceiling(dev, args.seed)
     if args.loop_steps > 0:
         result["loop"] = loop_leg(args.seed, args.loop_steps, dev)
     if args.cpu_seconds > 0 and W == "mixed":

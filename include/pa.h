@@ -148,6 +148,27 @@ pa_status pa_swap_blocks(const void *src_key_cache, const void *src_value_cache,
                          pa_dtype kv_dtype, hipStream_t stream);
 
 /*
+ * pa_read_probe - a measurement helper, not a step of the attention path: the
+ * HBM read bandwidth of decode's access pattern. Decode streams its K/V as
+ * 8 KiB (block, head) tiles gathered through the block table ([P2] s.1-2);
+ * this call reads the 8 KiB blocks order[0..num_blocks) of pool with the
+ * same non-temporal 16-byte loads, two blocks in flight per wavefront, and
+ * folds every word into a per-lane XOR. The identity order gives a plain
+ * streaming read, a random permutation the gather pattern.
+ *  pool        [device] pool_bytes bytes; block b is bytes [8192 b, 8192 b + 8192)
+ *  order       [device] int32 [num_blocks]; ids outside [0, pool_bytes / 8192)
+ *              are skipped (read as zeros, no access)
+ *  sink        [device] uint32 [sink_words], sink_words >= pa_read_probe_sink_words();
+ *              the first pa_read_probe_sink_words() words are overwritten, and
+ *              their XOR equals the XOR of all 32-bit words of the blocks read
+ * PA_EINVAL for negative sizes, null pointers or a short sink.
+ */
+int64_t pa_read_probe_sink_words(void);
+pa_status pa_read_probe(const void *pool, int64_t pool_bytes, const int32_t *order,
+                        int32_t num_blocks, uint32_t *sink, int64_t sink_words,
+                        hipStream_t stream);
+
+/*
  * pa_decode - single-pass paged decode attention: one query token per
  * sequence attends over its whole paged context ([P3] PagedAttention section:
  * the scattered blocks "appear contiguous to the attention mechanism").

@@ -8,6 +8,7 @@ it (``binding``). ``inputs`` holds the seeded synthetic workloads.
 from .binding import (BlockAllocator, PAError, pa_copy_blocks, pa_decode,  # noqa: F401
                       pa_decode_fp8, pa_decode_partitioned, pa_decode_partitioned_fp8,
                       pa_partition_workspace_bytes, pa_prefill_chunk, pa_reduce,
-                      pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_swap_blocks)
+                      pa_read_probe, pa_reshape_and_cache, pa_reshape_and_cache_fp8,
+                      pa_swap_blocks)
 
 __version__ = "0.1.0"

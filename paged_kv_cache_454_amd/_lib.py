@@ -58,6 +58,8 @@ SIGNATURES = {
     "pa_alloc_is_swapped": (_i32, [_p, _i64]),
     "pa_alloc_swap_out": (_st, [_p, _i64, _i32, _p, _p]),
     "pa_alloc_swap_in": (_st, [_p, _i64, _i32, _p, _p]),
+    "pa_read_probe_sink_words": (_i64, []),
+    "pa_read_probe": (_st, [_p, _i64, _p, _i32, _p, _i64, _p]),
 }
 
 _LIB = None

@@ -140,6 +140,22 @@ def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cach
         dt, _stream(stream)))
 
 
+def pa_read_probe(pool, order, sink=None, stream=None):
+    """Read the 8 KiB blocks ``order`` (int32, device) of ``pool`` (any device
+    tensor, its bytes taken as the pool) with decode's loads; returns the
+    uint32 sink whose XOR is the XOR of every word read. A measurement helper."""
+    n = int(lib().pa_read_probe_sink_words())
+    if sink is None:
+        sink = torch.empty(n, dtype=torch.int32, device=pool.device)
+    if order.dim() != 1:
+        raise ValueError("order must be int32 [num_blocks]")
+    check(lib().pa_read_probe(_dev(pool, "pool"), pool.numel() * pool.element_size(),
+                              _dev(order, "order", torch.int32), order.shape[0],
+                              _dev(sink, "sink"), sink.numel() * sink.element_size() // 4,
+                              _stream(stream)))
+    return sink
+
+
 def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
                              stream=None):
     """Quantising write: the E4M3 codes of key / k_scale and value / v_scale

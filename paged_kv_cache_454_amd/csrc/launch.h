@@ -75,6 +75,11 @@ bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 // not covered.
 bool launch_decode_fp8(const DecodeParams &p, hipStream_t stream);
 
+// HBM read probe: 8 KiB blocks of a pool in the given order (see read_probe.hip).
+int64_t read_probe_sink_words();
+pa_status launch_read_probe(const void *pool, int64_t pool_bytes, const int32_t *order,
+                            int32_t num_blocks, uint32_t *sink, hipStream_t stream);
+
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

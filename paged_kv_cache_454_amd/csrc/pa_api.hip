@@ -182,6 +182,25 @@ extern "C" pa_status pa_swap_blocks(const void *src_key_cache, const void *src_v
                                 dst_num_blocks, src_key_cache == dst_key_cache, fn, stream);
 }
 
+extern "C" int64_t pa_read_probe_sink_words(void) { return pa::read_probe_sink_words(); }
+
+extern "C" pa_status pa_read_probe(const void *pool, int64_t pool_bytes, const int32_t *order,
+                                   int32_t num_blocks, uint32_t *sink, int64_t sink_words,
+                                   hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_read_probe";
+  if (num_blocks < 0 || pool_bytes < 0 || sink_words < 0)
+    return pa::fail(PA_EINVAL, "%s: num_blocks=%d pool_bytes=%lld sink_words=%lld", fn,
+                    num_blocks, (long long)pool_bytes, (long long)sink_words);
+  if (!sink) return pa::fail(PA_EINVAL, "%s: sink is NULL", fn);
+  const int64_t need = pa::read_probe_sink_words();
+  if (sink_words < need)
+    return pa::fail(PA_EINVAL, "%s: sink has %lld words, needs %lld", fn, (long long)sink_words,
+                    (long long)need);
+  if (num_blocks > 0 && (!pool || !order)) return pa::fail(PA_EINVAL, "%s: null pointer", fn);
+  return pa::launch_read_probe(pool, pool_bytes, order, num_blocks, sink, stream);
+}
+
 extern "C" pa_status pa_decode(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

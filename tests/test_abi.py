@@ -167,3 +167,14 @@ def test_swap_blocks_rejects_bad_arguments():
     assert sw() == _lib.PA_EINVAL and b"null" in lib.pa_last_error()
     assert sw(n=0) == _lib.PA_OK                                    # no pairs: no-op
     assert sw(n=0, dt=_lib.PA_FP8_E4M3) == _lib.PA_OK
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = _lib.lib()
+    fake = ctypes.c_void_p(16)          # never dereferenced: validation fails first
+    assert lib.pa_read_probe(NULL, 0, NULL, -1, fake, 1 << 20, NULL) == _lib.PA_EINVAL
+    assert lib.pa_read_probe(NULL, -5, NULL, 0, fake, 1 << 20, NULL) == _lib.PA_EINVAL
+    assert lib.pa_read_probe(NULL, 0, NULL, 0, NULL, 1 << 20, NULL) == _lib.PA_EINVAL
+    assert lib.pa_read_probe(fake, 8192, NULL, 4, fake, 1 << 20, NULL) == _lib.PA_EINVAL
+    st = lib.pa_read_probe(fake, 8192, fake, 4, fake, 10, NULL)
+    assert st == _lib.PA_EINVAL and b"sink" in lib.pa_last_error()
