@@ -60,9 +60,9 @@ PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", 
 # tokens; for the others it is the fastest measured on MI355X (mixed
 # 16-layer step with the matrix-core decode: 1.406 ms at 512, 1.348 ms at
 # 1024, 1.311 ms at 2048, 1.822 ms at 4096, where too few units are left to
-# balance the CUs). The FP8 leg keeps 1024, its measured best.
+# balance the CUs). The FP8 leg: 1.005 ms at 512, 0.928 ms at 1024, 0.916 ms at 2048.
 DEFAULT_PARTITION = {"mixed": 2048, "long": 512, "uniform": 256}
-FP8_DEFAULT_PARTITION = {"mixed": 1024, "long": 512, "uniform": 256}
+FP8_DEFAULT_PARTITION = {"mixed": 2048, "long": 512, "uniform": 256}
 WORKLOAD_NAMES = {
     "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
     "long": "long-context split decode, 4 seqs {8192, 16384, 32768, 32768}, bs 32",
@@ -91,7 +91,7 @@ def parse():
     ap.add_argument("--fp8", type=int, default=1,
                     help="also time the step over FP8 (E4M3FN) pools (0: skip)")
     ap.add_argument("--fp8-partition-size", type=int, default=None,
-                    help="partition size of the FP8 leg (default: 1024 for the mixed workload, "
+                    help="partition size of the FP8 leg (default: 2048 for the mixed workload, "
                          "512 for the long one, 256 for the uniform one)")
     ap.add_argument("--loop-steps", type=int, default=50,
                     help="timed iterations of the continuous-batching loop leg (0 skips it)")
