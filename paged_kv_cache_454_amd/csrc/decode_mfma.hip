@@ -464,43 +464,59 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int w = 0; w < NW; ++w) anybad |= mg_bad[w];
     const bool bad = anybad != 0;
 
-    // All waves merge the unit's 8 partial states and store it. Every
-    // thread issues the same, fixed number of buffer stores (stores that
-    // must not happen get an offset past num_records and are dropped), which
-    // keeps the compiler's wait counts exact for the loads in flight.
+    // All waves merge the unit's 8 partial states and store it: thread t
+    // takes channels 4t .. 4t+3 of the unit's G x 256 outputs (float4 LDS
+    // reads and 16-byte stores). Every thread issues the same, fixed number
+    // of buffer stores (stores that must not happen get an offset past
+    // num_records and are dropped), which keeps the compiler's wait counts
+    // exact for the loads in flight.
+    static_assert(G * D / 4 <= NW * 64, "one channel quad per thread");
     const int64_t qrow = (int64_t)uj.x * HQ + (int64_t)uj.y * G;
     const int part = __builtin_amdgcn_readfirstlane(ubadpart[j]) >> 1;
-    constexpr int ITER = (G * D + NW * 64 - 1) / (NW * 64);
-#pragma unroll 1
-    for (int it = 0; it < ITER; ++it) {
-      const int idx = threadIdx.x + it * NW * 64;
+    {
+      const int idx = 4 * threadIdx.x;
       const bool live = idx < G * D;
       const int h = live ? idx / D : 0;
       const int ch = idx - h * D;
       float M = kNoMax;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, mg_m[w][h]);
-      float L = 0.f, A = 0.f;
+      float L = 0.f;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(mg_m[w][h] - M);
         L += mg_l[w][h] * f;
-        A += reinterpret_cast<const float *>(vbuf_all[w])[live ? idx : 0] * f;
+        const float4 a = *reinterpret_cast<const float4 *>(
+            reinterpret_cast<const float *>(vbuf_all[w]) + (live ? idx : 0));
+        A.x += a.x * f;
+        A.y += a.y * f;
+        A.z += a.z * f;
+        A.w += a.w * f;
       }
+      const float inv = SPLIT ? 1.f / L : (L > 0.f ? 1.f / L : 0.f);
+      const float4 ov = bad ? make_float4(nan, nan, nan, nan)
+                            : make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+      u32x4 ob;
+      ob[0] = __float_as_uint(ov.x);
+      ob[1] = __float_as_uint(ov.y);
+      ob[2] = __float_as_uint(ov.z);
+      ob[3] = __float_as_uint(ov.w);
       constexpr int kDrop = 0x7ffffff0;
       if constexpr (!SPLIT) {
-        const float ov = bad ? nan : (L > 0.f ? A / L : 0.f);
         const int64_t e = (qrow + h) * D + ch;
-        if (p.out_bf16)
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(ov), out_rsrc,
-                                                live ? (int)(e * 2) : kDrop, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), out_rsrc,
-                                                live ? (int)(e * 4) : kDrop, 0, 0);
+        if (p.out_bf16) {
+          u32x2 b2;
+          b2[0] = (uint32_t)f32_to_bf16(ov.x) | ((uint32_t)f32_to_bf16(ov.y) << 16);
+          b2[1] = (uint32_t)f32_to_bf16(ov.z) | ((uint32_t)f32_to_bf16(ov.w) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b2, out_rsrc, live ? (int)(e * 2) : kDrop, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(ob, out_rsrc, live ? (int)(e * 4) : kDrop, 0, 0);
+        }
       } else {
         const int64_t pidx = (qrow + h) * p.max_parts + part;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bad ? nan : A / L), out_rsrc,
-                                              live ? (int)((pidx * D + ch) * 4) : kDrop, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(ob, out_rsrc,
+                                               live ? (int)((pidx * D + ch) * 4) : kDrop, 0, 0);
         const int moff = (live && ch == 0) ? (int)(pidx * 4) : kDrop;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bad ? nan : M * kLn2), max_rsrc,
                                               moff, 0, 0);
