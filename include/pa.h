@@ -324,7 +324,7 @@ pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *
  * points (pa_reduce merges the partitions). Codes widen to BF16 exactly;
  * the K scale is applied to the logits and the V scale to the outputs, in
  * fp32. Supported shapes as pa_decode (head_dim 64/128/256, groups <= 8);
- * head_dim 256 with block_size a multiple of 16 takes the persistent kernel.
+ * head_dim 256 with block_size a multiple of 16 takes the persistent matrix-core kernel.
  */
 pa_status pa_decode_fp8(void *out, const void *query, const uint8_t *key_cache,
                         const uint8_t *value_cache, const int32_t *block_tables,
