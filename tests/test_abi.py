@@ -178,3 +178,13 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.pa_read_probe(fake, 8192, NULL, 4, fake, 1 << 20, NULL) == _lib.PA_EINVAL
     st = lib.pa_read_probe(fake, 8192, fake, 4, fake, 10, NULL)
     assert st == _lib.PA_EINVAL and b"sink" in lib.pa_last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; --gpus N > 1 exits with a message (checked
+    before anything touches a GPU)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
