@@ -7,7 +7,7 @@ the needed size - run as 16 independent layers back to back.
 
 One step = for each of the 16 layers: the slot-mapped write of the step's
 new K/V (pa_reshape_and_cache), split-context decode (pa_decode_partitioned,
-2048-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
+1792-token partitions) and the log-sum-exp merge (pa_reduce). Block tables and
 slot mappings come from the host allocator's layout before timing starts;
 every input is resident in HBM when the timed region begins.
 
@@ -58,10 +58,11 @@ PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", 
                            for f in ("prefill_mfma.hip", "pa_device.h")]
 # Partition size per workload: the long-context configuration fixes 512
 # tokens; for the others it is the fastest measured on MI355X (mixed
-# 16-layer step with the matrix-core decode: 1.406 ms at 512, 1.348 ms at
-# 1024, 1.311 ms at 2048, 1.822 ms at 4096, where too few units are left to
-# balance the CUs). The FP8 leg: 1.005 ms at 512, 0.928 ms at 1024, 0.916 ms at 2048.
-DEFAULT_PARTITION = {"mixed": 2048, "long": 512, "uniform": 256}
+# 16-layer step with the matrix-core decode: 1.335 ms at 1536, 1.281-1.284
+# ms at 1792, 1.297-1.303 ms at 2048, 1.822 ms at 4096, where too few units
+# are left to balance the CUs). The FP8 leg: 1.005 ms at 512, 0.928 ms at
+# 1024, 0.931 ms at 1792, 0.915 ms at 2048.
+DEFAULT_PARTITION = {"mixed": 1792, "long": 512, "uniform": 256}
 FP8_DEFAULT_PARTITION = {"mixed": 2048, "long": 512, "uniform": 256}
 WORKLOAD_NAMES = {
     "mixed": "mixed-length multi-tenant decode, 64 seqs log-uniform [16, 8192], 16 layers",
@@ -77,7 +78,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="split-context partition in tokens (default: 2048 for the mixed "
+                    help="split-context partition in tokens (default: 1792 for the mixed "
                          "workload, 512 for the long one as its configuration states, 256 "
                          "for the uniform one)")
     ap.add_argument("--workload", default="mixed", choices=["mixed", "long", "uniform"],
