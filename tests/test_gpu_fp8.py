@@ -249,3 +249,24 @@ def test_degenerate_and_poisoned_fp8():
     assert np.isnan(out_p[0]).all() and np.isnan(out_p[2]).all()
     assert G.max_err(out_p[1], good[1]) <= G.BF16_TOL
     assert np.all(out_p[3] == 0)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 5, 7])
+def test_fp8_matrix_core_groups(group):
+    """The FP8 matrix-core kernel at the group sizes the shapes above do not
+    reach (its MFMA columns beyond the group repeat real heads): single pass
+    and 256-token partitions, ragged contexts over many tiles, block size 16."""
+    print(f"[fp8] matrix-core group={group}", flush=True)
+    rng = np.random.default_rng(70 + group)
+    lens = [int(x) for x in rng.integers(1, 2048, size=12)]
+    lens[0] = 2048
+    case = inputs.decode_case(lens, 2 * group, 2, 256, 16, dtype="bf16", pool_factor=1.2,
+                              seed=group)
+    t, kc, vc = _fp8_case(case)
+    _write(t)
+    okc, ovc = _oracle_pools(case, kc, vc)
+    want = oracle.decode(case.query, okc, ovc, case.block_tables, case.context_lens, 16,
+                         case.scale, KS, VS)
+    assert G.max_err(G.host(_decode(t, case)), want) <= G.BF16_TOL
+    got, *_ = _partitioned(t, case, 256)
+    assert G.max_err(G.host(got), want) <= G.BF16_TOL
