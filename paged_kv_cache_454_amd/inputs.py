@@ -16,13 +16,16 @@ case, in the order written in :func:`decode_case` / :func:`prefill_case`):
               Throughput LLM Inference & Training" (Fig. 1 / Fig. 2).
 * ``uniform`` bf16, 8 sequences x 2048 tokens, 24/4 heads, head_dim 256,
               block_size 16, pool exactly the blocks needed, seeded order.
+              One layer; timed over 8 independent pool sets in turn (8 x 64
+              MiB), so that repeated steps cannot be served from the caches.
 * ``mixed``   bf16, 64 sequences, lengths floor(exp(U(ln 16, ln 8192))),
               24/4/256, block_size 16, pool 1.5x the blocks needed with the
               sequences' blocks scattered at random; unused blocks are garbage.
               Run as 16 independent layers back to back.
 * ``long``    bf16, 4 sequences of 8192/16384/32768/32768 tokens, 24/4/256,
               block_size 32, 512-token partitions; K and V are N(0,1) plus a
-              per-(KV head, channel) bias drawn N(0, 3^2).
+              per-(KV head, channel) bias drawn N(0, 3^2). One layer;
+              timed over 3 independent pool sets in turn (3 x 352 MiB).
 * ``prefill`` bf16, 16 sequences with an existing context drawn uniformly
               from 0..6000 tokens plus a 512-token query chunk, 24/4/256,
               block_size 16.
@@ -42,13 +45,13 @@ PRESETS = {
     "tiny": dict(kind="decode", dtype="f32", context_lens=[3, 5, 2], num_q_heads=4,
                  num_kv_heads=1, head_dim=64, block_size=4, num_blocks=8, scale=1.0 / 8.0),
     "uniform": dict(kind="decode", dtype="bf16", context_lens=[2048] * 8, num_q_heads=24,
-                    num_kv_heads=4, head_dim=256, block_size=16, pool_factor=1.0),
+                    num_kv_heads=4, head_dim=256, block_size=16, pool_factor=1.0, pool_sets=8),
     "mixed": dict(kind="decode", dtype="bf16", num_seqs=64, min_len=16, max_len=8192,
                   num_q_heads=24, num_kv_heads=4, head_dim=256, block_size=16,
                   pool_factor=1.5, layers=16),
     "long": dict(kind="decode", dtype="bf16", context_lens=[8192, 16384, 32768, 32768],
                  num_q_heads=24, num_kv_heads=4, head_dim=256, block_size=32,
-                 pool_factor=1.0, kv_bias_scale=3.0, partition_size=512),
+                 pool_factor=1.0, kv_bias_scale=3.0, partition_size=512, pool_sets=3),
     "prefill": dict(kind="prefill", dtype="bf16", num_seqs=16, max_existing=6000, chunk=512,
                     num_q_heads=24, num_kv_heads=4, head_dim=256, block_size=16),
 }
