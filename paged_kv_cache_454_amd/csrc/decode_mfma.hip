@@ -61,6 +61,12 @@ constexpr int KL = 8;       // 16-byte K loads per lane per tile
 constexpr int VL = 8;       // 16-byte V loads per lane per tile
 constexpr int VROW = 544;   // bytes per token row of a wave's LDS V buffer
 constexpr int VBUF = TILE * VROW;
+// LDS row strides padded by 16 bytes so that the rows of different query
+// heads start on different banks: a query row of 32 x 16 bytes (read 16
+// lanes at a time, one head per lane, the same channels) and a parked merge
+// row of D floats (written one head per lane).
+constexpr int QROW = 33;      // uint4 per query row
+constexpr int RSTR = D + 4;   // floats per parked merge row
 constexpr float kLazy = 8.f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -118,10 +124,10 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 template <int G>
 struct CfgM {
   static constexpr int FIXED = NW * VBUF + 4096;
-  static constexpr int NQ_FIT = (150 * 1024 - FIXED) / (G * 32 * 16);
+  static constexpr int NQ_FIT = (150 * 1024 - FIXED) / (G * QROW * 16);
   static constexpr int NQ = NQ_FIT > 32 ? 32 : NQ_FIT;  // query slots in LDS
   static_assert(NQ >= 4, "too little LDS left for the query slots");
-  static_assert(G * D * 4 <= VBUF, "a wave's merge state must fit its V buffer");
+  static_assert(G * RSTR * 4 <= VBUF, "a wave's merge state must fit its V buffer");
   static_assert(VBUF >= 192 * 4, "the planner needs 192 ints of scratch");
 };
 
@@ -139,11 +145,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(DecodeParams p) {
   using C = CfgM<G>;
   // Per wave: the V tile being consumed, then (at a unit's end) the wave's
-  // merge state [G][D] floats.
+  // merge state [G][RSTR] floats.
   __shared__ __attribute__((aligned(16))) uint8_t vbuf_all[NW][VBUF];
   __shared__ float mg_m[NW][8], mg_l[NW][8];
   __shared__ int mg_bad[NW];
-  __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][32];
+  __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
   __shared__ int ubadpart[MAXU];   // part * 2 + bad
   __shared__ uint32_t act_lds[2];
@@ -450,7 +456,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (live_head) {
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb)
-        *reinterpret_cast<float4 *>(&red[n16 * D + 16 * cb + 4 * grp]) =
+        *reinterpret_cast<float4 *>(&red[n16 * RSTR + 16 * cb + 4 * grp]) =
             make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
       if (grp == 0) {
         mg_m[wave][n16] = m_run;
@@ -488,7 +494,7 @@ void decode_mfma_kernel(DecodeParams p) {
         const float f = fast_exp2(mg_m[w][h] - M);
         L += mg_l[w][h] * f;
         const float4 a = *reinterpret_cast<const float4 *>(
-            reinterpret_cast<const float *>(vbuf_all[w]) + (live ? idx : 0));
+            reinterpret_cast<const float *>(vbuf_all[w]) + (live ? h * RSTR + ch : 0));
         A.x += a.x * f;
         A.y += a.y * f;
         A.z += a.z * f;
