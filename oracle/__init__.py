@@ -25,11 +25,14 @@ Modules:
 * ``accounting`` - the KV-size closed form and the reservation counts of the
   contiguous and paged policies (pinned by the pages' printed numbers).
 * ``allocator``  - a model of the on-demand block allocator with a FIFO free
-  list (pinned by the worked example and the pages' stated invariants).
+  list (pinned by the worked example, the pages' stated invariants and
+  fixed-id block-table rows with a partly filled last block and -1 padding).
 * ``fp8``        - E4M3 codes (a stated choice; the pages define no quantised
-  cache), the quantising cache write and decode over the dequantised cache
-  (pinned by known codes, the full code table, torch's float8_e4m3fn
-  conversion and tie cases).
+  cache), the quantising cache write and decode (single pass and per
+  partition) over the dequantised cache (pinned by known codes, the full code
+  table, torch's float8_e4m3fn conversion, tie cases, and a brute-force loop
+  that dequantises each code through torch and reads the transposed value
+  pool directly, with unequal key and value scales).
 * ``attention``  - the slot-mapped cache write, logical reassembly of a paged
   cache, dense softmax decode attention, split-context partitions and their
   log-sum-exp merge, and causal chunked prefill (pinned by brute force,

@@ -229,6 +229,31 @@ def pin_allocator_invariants(alloc):
     assert b.num_free() == 0 and 2 not in b.tables
 
 
+def pin_block_table_rows(alloc):
+    """The exported block-table rows against fixed ids: a partly filled last
+    block, padding with -1 past the table ("vLLM Architecture, Memory and
+    Benchmarks Deep Dive", s.2: a block table maps each sequence's logical
+    blocks to physical ones; unused entries hold no block), and the lengths
+    are the tokens held, not whole blocks."""
+    order = [5, 2, 7, 0, 3, 6, 1, 4]
+    a = alloc.BlockAllocatorModel(8, 4, initial_order=order)
+    a.append(10, 6)          # blocks 5, 2: the second holds 2 of 4 slots
+    a.append(11, 1)          # block 7, 1 of 4 slots
+    a.append(12, 8)          # blocks 0, 3: both full
+    rows, lens = a.block_table([11, 10, 12], 4)
+    assert rows == [[7, -1, -1, -1], [5, 2, -1, -1], [0, 3, -1, -1]], rows
+    assert lens == [1, 6, 8], lens
+    a.append(10, 3)          # fills block 2 and takes block 6 for the ninth token
+    rows, lens = a.block_table([10], 3)
+    assert rows == [[5, 2, 6]] and lens == [9], (rows, lens)
+    try:
+        a.block_table([10], 2)   # three blocks do not fit a two-entry row
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a row shorter than the table must be refused")
+
+
 def _cow_state_ok(a):
     held = {}
     for table in a.tables.values():
@@ -761,6 +786,51 @@ def pin_fp8_cache(fp8):
     assert np.abs(got - want).max() < 1e-12
 
 
+def pin_fp8_partitions(fp8):
+    """Per-partition FP8 records against a brute-force loop: every code is
+    dequantised on its own through torch's float8_e4m3fn (a library
+    conversion), keys read from the row layout [nb][H][bs][d] and values from
+    the transposed block layout [nb][H][d][bs]; unequal key and value scales,
+    so a swap of the two changes the logits and the outputs."""
+    import torch
+    rng = np.random.default_rng(37)
+    nb, hkv, hq, bs, d, P = 10, 2, 6, 4, 6, 4   # d != bs: the value layout matters
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes_k = rng.choice(finite, size=(nb, hkv, bs, d))
+    codes_v = rng.choice(finite, size=(nb, hkv, d, bs))
+    q = rng.standard_normal((3, hq, d)) * 0.05
+    tables = np.array([[4, 9, 1], [7, -1, -1], [0, 5, 8]])
+    lens = np.array([9, 3, 12])
+    scale, ks, vs = 0.4, 0.03, 1.7
+
+    def deq(c, sc):
+        t = torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn)
+        return float(t.to(torch.float64)[0]) * float(np.float32(sc))
+
+    o, lse, n = fp8.decode_partitions(q, codes_k, codes_v, tables, lens, bs, scale, ks, vs, P)
+    assert list(n) == [3, 1, 3]
+    for s in range(3):
+        T = int(lens[s])
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for p in range(-(-T // P)):
+                toks = range(p * P, min(T, (p + 1) * P))
+                z = []
+                for t in toks:
+                    blk, off = int(tables[s][t // bs]), t % bs
+                    z.append(scale * sum(float(q[s, h, c]) * deq(codes_k[blk, g, off, c], ks)
+                                         for c in range(d)))
+                top = max(z)
+                tot = sum(math.exp(v - top) for v in z)
+                assert abs(lse[s, h, p] - (top + math.log(tot))) < 1e-12
+                for c in range(d):
+                    acc = 0.0
+                    for t, v in zip(toks, z):
+                        blk, off = int(tables[s][t // bs]), t % bs
+                        acc += math.exp(v - top) * deq(codes_v[blk, g, c, off], vs)
+                    assert abs(o[s, h, p, c] - acc / tot) < 1e-12 * max(1.0, abs(acc / tot))
+
+
 def attention_decode_ref(q, kc, vc, tables, lens, bs, scale, v_tokens_last=False):
     """Brute-force decode (loops), for the fp8 pin; v_tokens_last: the value
     pool is [nb][H][d][bs]."""
@@ -787,6 +857,6 @@ ATTENTION_PINS = [pin_cache_write, pin_decode_bruteforce, pin_decode_vs_library,
                   pin_decode_special_cases, pin_permutation_invariance, pin_partitions,
                   pin_prefill, pin_copy_blocks, pin_swap_blocks]
 ACCOUNTING_PINS = [pin_kv_size, pin_worked_example_accounting]
-FP8_PINS = [pin_fp8_codes, pin_fp8_cache]
+FP8_PINS = [pin_fp8_codes, pin_fp8_cache, pin_fp8_partitions]
 ALLOCATOR_PINS = [pin_worked_example_allocator, pin_allocator_invariants, pin_cow_contents,
-                  pin_cow_counts, pin_swap_contents, pin_swap_counts]
+                  pin_cow_counts, pin_swap_contents, pin_swap_counts, pin_block_table_rows]

@@ -104,6 +104,20 @@ MUTATIONS += [
      "        if not (0 <= src < nd and 0 <= dst < ns):\n            continue\n        kd[dst]"),
 ]
 
+MUTATIONS += [
+    # split-context decode over FP8 pools: the value pool read untransposed,
+    # and the key and value scales exchanged
+    ("fp8", "dequantize(key_codes, k_scale),\n                                       dequantize(value_rows(value_codes), v_scale), block_tables,\n                                       context_lens, block_size, scale, partition_size,",
+     "dequantize(key_codes, k_scale),\n                                       dequantize(value_codes, v_scale), block_tables,\n                                       context_lens, block_size, scale, partition_size,"),
+    ("fp8", "dequantize(key_codes, k_scale),\n                                       dequantize(value_rows(value_codes), v_scale), block_tables,\n                                       context_lens, block_size, scale, partition_size,",
+     "dequantize(key_codes, v_scale),\n                                       dequantize(value_rows(value_codes), k_scale), block_tables,\n                                       context_lens, block_size, scale, partition_size,"),
+    # exported block-table rows: padding and lengths
+    ("allocator", "def block_table(self, seq_ids, max_blocks, pad=-1):",
+     "def block_table(self, seq_ids, max_blocks, pad=0):"),
+    ("allocator", "            lens.append(self.lengths[sid])",
+     "            lens.append(len(t) * self.block_size)"),
+]
+
 PINS = {"attention": P.ATTENTION_PINS, "accounting": P.ACCOUNTING_PINS,
         "allocator": P.ALLOCATOR_PINS, "fp8": P.FP8_PINS}
 
