@@ -45,17 +45,25 @@ import time
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix cores, vendor figure
 HERE = os.path.dirname(os.path.abspath(__file__))
-# HBM bytes per decode launch, measured with FETCH_SIZE / WRITE_SIZE counters
-# and scaled by the same counters' reading for a plain copy of known size.
-TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_mfma_mixed_64seq_hbm_counters.md")
-TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
-                   for f in ("decode_mfma.hip", "pa_device.h", "persistent_plan.h")]
-FP8_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "decode_fp8_mixed_64seq_16layer.md")
-FP8_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
-                       for f in ("decode_fp8.hip", "pa_device.h", "persistent_plan.h")]
+# HBM bytes per launch, measured with FETCH_SIZE / WRITE_SIZE counters and
+# scaled by the same counters' reading for a plain copy of known size: one
+# record per (kernel leg, workload), each keyed to the sha256 of the sources
+# of the kernel it measured (a changed kernel reports null).
+_CSRC = os.path.join(HERE, "paged_kv_cache_454_amd", "csrc")
+_DECODE_SRC = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "pa_device.h",
+                                                "persistent_plan.h")]
+_TILED_SRC = [os.path.join(_CSRC, f) for f in ("decode_tiled.hip", "pa_device.h")]
+_FP8_SRC = [os.path.join(_CSRC, f) for f in ("decode_fp8.hip", "pa_device.h",
+                                             "persistent_plan.h")]
+TRAFFIC_RECORDS = {
+    ("bf16", "mixed"): ("decode_mfma_mixed_64seq_hbm_counters.md", _DECODE_SRC),
+    ("bf16", "long"): ("decode_mfma_long_4seq_hbm_counters.md", _DECODE_SRC),
+    ("bf16", "uniform"): ("decode_tiled_uniform_8x2048_hbm_counters.md", _TILED_SRC),
+    ("fp8", "mixed"): ("decode_fp8_mixed_64seq_16layer.md", _FP8_SRC),
+    ("fp8", "long"): ("decode_fp8_long_4seq_hbm_counters.md", _FP8_SRC),
+}
 PREFILL_TRAFFIC_RECORD = os.path.join(HERE, "profiles", "prefill_mfma_chunked_16x512.md")
-PREFILL_TRAFFIC_SOURCES = [os.path.join(HERE, "paged_kv_cache_454_amd", "csrc", f)
-                           for f in ("prefill_mfma.hip", "pa_device.h")]
+PREFILL_TRAFFIC_SOURCES = [os.path.join(_CSRC, f) for f in ("prefill_mfma.hip", "pa_device.h")]
 # Partition size per workload: the long-context configuration fixes 512
 # tokens; for the others it is the fastest measured on MI355X (mixed
 # 16-layer step with the matrix-core decode: 1.335 ms at 1536, 1.281-1.284
@@ -95,6 +103,9 @@ def parse():
     ap.add_argument("--fp8-partition-size", type=int, default=None,
                     help="partition size of the FP8 leg (default: 2048 for the mixed workload, "
                          "512 for the long one, 256 for the uniform one)")
+    ap.add_argument("--side-decode", type=int, default=1,
+                    help="with the mixed workload, also time the long-context and uniform "
+                         "decode workloads (0: skip)")
     ap.add_argument("--loop-steps", type=int, default=50,
                     help="timed iterations of the continuous-batching loop leg (0 skips it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
@@ -103,43 +114,59 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(seed, budget_s):
-    """Time the fp64 oracle (write + decode) on whole sequences of one layer of
+def cpu_baseline(seed, budget_s, single_core_s=6.0):
+    """Time the fp64 oracle (write + decode) on whole passes over one layer of
     the same workload until the budget is spent; GB/s over the same
-    algorithmic KV bytes as the GPU figure."""
+    algorithmic KV bytes as the GPU figure. Runs with the BLAS thread pool as
+    the process gets it (``cores`` = its size, the threads actually used),
+    then once more limited to one thread."""
     from oracle import attention as oracle
     from paged_kv_cache_454_amd import inputs
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
     case = inputs.preset_case("mixed", seed=seed, garbage="random")
-    t0 = time.perf_counter()
-    done_tokens, done_seqs, passes = 0, 0, 0
-    while True:   # whole passes over the layer (write + decode of every sequence)
-        kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
-                                    case.slot_mapping, case.block_size)
-        oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens,
-                      case.block_size, case.scale)
-        done_tokens += int(case.context_lens.sum())
-        done_seqs += case.num_seqs
-        passes += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    gbs = done_tokens * 4096 / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} pass(es) over 1 layer of the mixed workload (slot write + "
-                      f"fp64 decode of all {case.num_seqs} sequences, {done_tokens} context "
-                      f"tokens in total) in {dt:.1f} s; decode tokens/s for a 16-layer step "
-                      f"{done_seqs / dt / 16:.3f}"}
+
+    def run(budget):
+        t0 = time.perf_counter()
+        done_tokens, done_seqs, passes = 0, 0, 0
+        while True:   # whole passes over the layer (write + decode of every sequence)
+            kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
+                                        case.slot_mapping, case.block_size)
+            oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens,
+                          case.block_size, case.scale)
+            done_tokens += int(case.context_lens.sum())
+            done_seqs += case.num_seqs
+            passes += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        dt = time.perf_counter() - t0
+        return done_tokens * 4096 / dt / 1e9, passes, done_tokens, done_seqs, dt
+
+    gbs, passes, done_tokens, done_seqs, dt = run(budget_s)
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{passes} pass(es) over 1 layer of the mixed workload (slot write + "
+                     f"fp64 decode of all {case.num_seqs} sequences, {done_tokens} context "
+                     f"tokens in total) in {dt:.1f} s; decode tokens/s for a 16-layer step "
+                     f"{done_seqs / dt / 16:.3f}",
+           "host_cpus": os.cpu_count(),
+           "cpu_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+           else None}
+    if threadpool_limits is not None and single_core_s > 0:
+        with threadpool_limits(limits=1):
+            g1, p1, _, s1, d1 = run(single_core_s)
+        res["single_core"] = {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{p1} pass(es) of the same layer in {d1:.1f} s"}
+    return res
 
 
-def counted_traffic(workload, partition_size, seed, record=TRAFFIC_RECORD,
-                    sources=TRAFFIC_SOURCES):
-    """A counter record's HBM bytes per launch, or None when the record was
-    taken on another workload or the kernel's source has changed since."""
+def counted_traffic(workload, partition_size, seed, record, sources):
+    """A counter record's HBM bytes per launch, or None when the record is
+    missing, was taken on another workload, or the kernel's source has
+    changed since."""
     try:
         text = open(record).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
@@ -153,6 +180,14 @@ def counted_traffic(workload, partition_size, seed, record=TRAFFIC_RECORD,
             or rec.get("partition_size") != partition_size or rec.get("seed") != seed):
         return None
     return int(rec["traffic_bytes"])
+
+
+def decode_traffic(kind, workload, partition_size, seed):
+    if (kind, workload) not in TRAFFIC_RECORDS:
+        return None
+    name, sources = TRAFFIC_RECORDS[(kind, workload)]
+    return counted_traffic(workload, partition_size, seed, os.path.join(HERE, "profiles", name),
+                           sources)
 
 
 def timed_launches(fn, reps, stream):
@@ -462,7 +497,9 @@ def loop_leg(seed, steps, dev):
     }
 
 
-FP8_SCALES = (0.0375, 0.021)   # k_scale, v_scale of the FP8 pools (N(0,1) data)
+# k_scale, v_scale of the FP8 pools: N(0,1) data uses codes up to ~200; the
+# long-context batch adds a per-head bias of scale 3 (|x| up to ~16).
+FP8_SCALES = {"mixed": (0.0375, 0.021), "uniform": (0.0375, 0.021), "long": (0.05, 0.05)}
 
 
 def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
@@ -474,7 +511,10 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     import torch
 
     import paged_kv_cache_454_amd as pa
-    ks, vs = FP8_SCALES
+    from paged_kv_cache_454_amd import inputs
+    ks, vs = FP8_SCALES[workload]
+    # new tokens per step: one per sequence per independent copy of the layer
+    sets = len(layers) // inputs.PRESETS[workload].get("layers", 1)
 
     def codes(x, sc):
         return (x.float() / sc).to(torch.float8_e4m3fn).view(torch.uint8)
@@ -524,47 +564,41 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     del pools, po, pm, ps, outs
     torch.cuda.empty_cache()
     return {
-        "what": "the decode step over FP8 E4M3FN pools (scales k 0.0375, v 0.021): per layer "
+        "what": f"the decode step over FP8 E4M3FN pools (scales k {ks}, v {vs}): per pool set "
                 "pa_reshape_and_cache_fp8 + pa_decode_partitioned_fp8 + pa_reduce",
         "ms_per_step": round(ms_step, 5),
-        "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(S * sets / (ms_step * 1e-3), 1),
         "kv_gbs_effective": round(kv_bytes_layer * len(layers) / (ms_step * 1e-3) / 1e9, 2),
         "partition_size": P,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned_fp8",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic(workload, P, seed, FP8_TRAFFIC_RECORD,
-                                                FP8_TRAFFIC_SOURCES),
+                     "traffic": decode_traffic("fp8", workload, P, seed),
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is not implemented", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
+def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None):
+    """One decode workload at full size: K timed steps (per pool set: the
+    slot write of the step's new K/V, pa_decode_partitioned at partition
+    size P, pa_reduce) after W warm-up steps, then the decode kernel's own
+    launches timed back to back on the launch stream. Pool sets are the
+    mixed batch's 16 layers, or independent copies of a one-layer workload
+    decoded in turn so that no step re-reads K/V the last one left in the
+    caches. Returns the leg's figures (and the FP8 leg's, given fp8_P)."""
     import torch
 
     import paged_kv_cache_454_amd as pa
     from paged_kv_cache_454_amd import inputs
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    W = args.workload
-    # Independent pool sets decoded in turn: the layers of the mixed batch, or
-    # copies of a one-layer workload's pools (with their own queries), so
-    # that no step re-reads K/V that an earlier one left in the caches.
     pre = inputs.PRESETS[W]
     layers_n = pre.get("layers", pre.get("pool_sets", 1))
-    layers, meta = inputs.device_decode_layers(W, args.seed, layers_n, dev)
+    layers, meta = inputs.device_decode_layers(W, seed, layers_n, dev)
     lens = meta["lens"]
-    P = args.partition_size or DEFAULT_PARTITION[W]
     S = len(lens)
     hq, d = layers[0]["query"].shape[1], layers[0]["query"].shape[2]
+    hkv = pre["num_kv_heads"]
     max_parts = max(1, math.ceil(int(lens.max()) / P))
     po = torch.empty((S, hq, max_parts, d), dtype=torch.float32, device=dev)
     pm = torch.empty((S, hq, max_parts), dtype=torch.float32, device=dev)
@@ -586,67 +620,97 @@ def main():
             decode(li)
             pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
 
     # The decode kernel's own launches, timed in a separate pass (so the step
     # timing above carries no event overhead) on the stream they run on.
-    kern_ms = decode_launch_ms(decode, len(layers), max(3, min(args.steps, 20)), stream)
+    kern_ms = decode_launch_ms(decode, len(layers), max(3, min(steps, 20)), stream)
 
-    hkv = inputs.PRESETS[W]["num_kv_heads"]
     kv_bytes_layer = int(lens.sum()) * hkv * d * 2 * 2
     step_bytes = kv_bytes_layer * layers_n
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    tok_s = S / (ms_step * 1e-3)
     k_gbs = kv_bytes_layer / (kern_ms * 1e-3) / 1e9
+    res = {
+        "workload": WORKLOAD_NAMES[W],
+        "ms_per_step": round(ms_step, 5),
+        "tokens_per_s": round(S * (layers_n // pre.get("layers", 1)) / (ms_step * 1e-3), 1),
+        "kv_gbs_effective": round(gbs, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "config": {"num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
+                   "context_len_range": [int(lens.min()), int(lens.max())],
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                   "block_size": pre["block_size"], "pool_blocks": int(meta["num_blocks"]),
+                   "layers": pre.get("layers", 1), "pool_sets_per_step": layers_n,
+                   "partition_size": P, "seed": seed},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned",
+                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": decode_traffic("bf16", W, P, seed),
+                     "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": kv_bytes_layer},
+    }
+    if fp8_P:
+        del po, pm, ps, outs
+        res["fp8"] = fp8_leg(layers, meta, fp8_P, steps, warmup, dev, W, seed)
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = args.workload
+    P = args.partition_size or DEFAULT_PARTITION[W]
+    fp8_P = (args.fp8_partition_size or FP8_DEFAULT_PARTITION[W]) if args.fp8 else None
+    main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P)
 
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
-        "value": round(gbs, 2),
+        "value": main_leg["kv_gbs_effective"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": main_leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), rounded to BF16)",
-        "config": {"workload": WORKLOAD_NAMES[W],
-                   "num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
-                   "context_len_range": [int(lens.min()), int(lens.max())],
-                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
-                   "block_size": inputs.PRESETS[W]["block_size"],
-                   "pool_blocks": int(meta["num_blocks"]), "layers": pre.get("layers", 1),
-                   "pool_sets_per_step": layers_n,
-                   "partition_size": P, "seed": args.seed},
-        "tokens_per_s": round(tok_s, 1),
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned",
-                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic(W, P, args.seed),
-                     "avg_launch_us": round(kern_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": kv_bytes_layer},
+        "config": {"workload": main_leg["workload"], **main_leg["config"]},
+        "tokens_per_s": main_leg["tokens_per_s"],
+        "pct_of_hbm_peak": main_leg["pct_of_hbm_peak"],
+        "roofline": main_leg["roofline"],
     }
-    if args.fp8:
-        del po, pm, ps, outs
-        result["fp8"] = fp8_leg(layers, meta, args.fp8_partition_size or FP8_DEFAULT_PARTITION[W], args.steps,
-                                args.warmup, dev, W, args.seed)
+    if "fp8" in main_leg:
+        result["fp8"] = main_leg["fp8"]
+    # The other two decode configurations of the target (long-context split
+    # decode at its stated 512-token partitions; uniform batch), each with its
+    # own step time and kernel roofline; they do not enter `value`.
+    if args.side_decode and W == "mixed":
+        for w2 in ("long", "uniform"):
+            f2 = FP8_DEFAULT_PARTITION[w2] if (args.fp8 and w2 == "long") else None
+            result[w2] = decode_leg(w2, DEFAULT_PARTITION[w2], args.steps, args.warmup, dev,
+                                    args.seed, f2)
     if args.prefill_reps > 0:
-        del layers
-        if not args.fp8:
-            del po, pm, ps, outs
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
         result["cow"] = cow_leg(args.seed, args.prefill_reps, dev)

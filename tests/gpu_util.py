@@ -81,6 +81,26 @@ def partitioned(t, case, partition_size, out_dtype=torch.float32, max_parts=None
     return out, po, pm, ps
 
 
+def bench_partitions():
+    """The partition sizes bench.py times, per workload: (BF16, FP8) dicts.
+    Imported, not copied, so the parity tests run exactly what is timed."""
+    import bench
+    return bench.DEFAULT_PARTITION, bench.FP8_DEFAULT_PARTITION
+
+
+def check_records(po, pm, ps, o_want, lse_want, num_parts, tol=BF16_TOL, lse_tol=1e-3):
+    """Every partition record of every (sequence, query head): lse_p = m_p +
+    ln l_p and o_p against the oracle's (m_p and l_p alone are not unique)."""
+    po, pm, ps = host(po), host(pm), host(ps)
+    for s, k in enumerate(np.asarray(num_parts).tolist()):
+        if k == 0:
+            continue
+        lse_g = pm[s, :, :k] + np.log(ps[s, :, :k])
+        assert np.isfinite(lse_g).all(), s
+        assert np.abs(lse_g - lse_want[s, :, :k]).max() <= lse_tol, s
+        assert max_err(po[s, :, :k], o_want[s, :, :k]) <= tol, s
+
+
 def host(x):
     return x.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 

@@ -38,10 +38,10 @@ def _codes(x, scale):
     return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def _fp8_case(case):
+def _fp8_case(case, ks=KS, vs=VS):
     """Device tensors of a BF16 decode case with the pools as codes (the
     value pool in its transposed block layout [nb][H][d][bs])."""
-    kc, vc = _codes(case.key_cache, KS), _codes(np.swapaxes(case.value_cache, 2, 3), VS)
+    kc, vc = _codes(case.key_cache, ks), _codes(np.swapaxes(case.value_cache, 2, 3), vs)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(G.DEV)
     t = dict(key_cache=torch.from_numpy(kc).to(G.DEV), value_cache=torch.from_numpy(vc).to(G.DEV),
              key=bf(case.key), value=bf(case.value), query=bf(case.query),
@@ -51,31 +51,31 @@ def _fp8_case(case):
     return t, kc, vc
 
 
-def _write(t):
+def _write(t, ks=KS, vs=VS):
     pa.pa_reshape_and_cache_fp8(t["key"], t["value"], t["key_cache"], t["value_cache"],
-                                t["slot_mapping"], KS, VS)
+                                t["slot_mapping"], ks, vs)
 
 
-def _oracle_pools(case, kc, vc):
+def _oracle_pools(case, kc, vc, ks=KS, vs=VS):
     return oracle.cache_write(kc, vc, case.key, case.value, case.slot_mapping, case.block_size,
-                              KS, VS)
+                              ks, vs)
 
 
-def _decode(t, case, out_dtype=torch.float32):
+def _decode(t, case, out_dtype=torch.float32, ks=KS, vs=VS):
     out = torch.empty(tuple(t["query"].shape), dtype=out_dtype, device=G.DEV)
     pa.pa_decode_fp8(out, t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
-                     t["context_lens"], case.scale, KS, VS)
+                     t["context_lens"], case.scale, ks, vs)
     return out
 
 
-def _partitioned(t, case, P, max_parts=None):
+def _partitioned(t, case, P, max_parts=None, ks=KS, vs=VS):
     S, H, D = t["query"].shape
     n = max_parts or G.max_parts_for(case, P)
     po = torch.full((S, H, n, D), float("nan"), dtype=torch.float32, device=G.DEV)
     pm = torch.full((S, H, n), float("nan"), dtype=torch.float32, device=G.DEV)
     ps = torch.full((S, H, n), float("nan"), dtype=torch.float32, device=G.DEV)
     pa.pa_decode_partitioned_fp8(po, pm, ps, t["query"], t["key_cache"], t["value_cache"],
-                                 t["block_tables"], t["context_lens"], case.scale, KS, VS, P)
+                                 t["block_tables"], t["context_lens"], case.scale, ks, vs, P)
     out = torch.empty((S, H, D), dtype=torch.float32, device=G.DEV)
     pa.pa_reduce(out, po, pm, ps, t["context_lens"], P)
     return out, po, pm, ps
@@ -197,23 +197,53 @@ def test_partition_records_fp8():
 
 def test_mixed_full_size_fp8():
     """The mixed batch (64 sequences, 16..8192 tokens, 24/4 heads, d 256,
-    blocks of 16) with FP8 pools; sampled sequences against the oracle, and
-    single pass against partitions (512) on every row."""
+    blocks of 16) with FP8 pools, every sequence against the oracle: single
+    pass, and partitions at the size the benchmark's FP8 leg times, with
+    every partition record compared."""
     print("[fp8] preset=mixed", flush=True)
     case = inputs.preset_case("mixed", seed=0)
     t, kc, vc = _fp8_case(case)
     _write(t)
-    lens = case.context_lens
-    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 17, 33, 63})
     okc, ovc = _oracle_pools(case, kc, vc)
-    want = oracle.decode(case.query[sample], okc, ovc, case.block_tables[sample], lens[sample],
+    want = oracle.decode(case.query, okc, ovc, case.block_tables, case.context_lens,
                          case.block_size, case.scale, KS, VS)
-    single = G.host(_decode(t, case))
-    assert G.max_err(single[sample], want) <= G.BF16_TOL
-    got_p, *_ = _partitioned(t, case, 512)
-    got_p = G.host(got_p)
-    assert G.max_err(got_p[sample], want) <= G.BF16_TOL
-    assert G.max_err(single, got_p) <= G.BF16_TOL
+    assert G.max_err(G.host(_decode(t, case)), want) <= G.BF16_TOL
+    P = G.bench_partitions()[1]["mixed"]
+    got_p, po, pm, ps = _partitioned(t, case, P)
+    assert G.max_err(G.host(got_p), want) <= G.BF16_TOL
+    o_w, lse_w, n = oracle.decode_partitions(case.query, okc, ovc, case.block_tables,
+                                             case.context_lens, case.block_size, case.scale,
+                                             KS, VS, P)
+    G.check_records(po, pm, ps, o_w, lse_w, n)
+    again, *_ = _partitioned(t, case, P)
+    assert np.array_equal(G.bits(got_p), G.bits(again))
+
+
+# The long batch's keys and values carry a per-head bias of scale 3 (|x| up
+# to about 16), so its pools take scales that keep every code finite.
+KS_LONG, VS_LONG = 0.05, 0.05
+
+
+def test_long_full_size_fp8():
+    """The long-context batch (4 sequences, 8192..32768 tokens, blocks of 32)
+    with FP8 pools at full size: partitions at the size the benchmark's FP8
+    leg times, every record and the merged output against the oracle, and
+    the single pass."""
+    print("[fp8] preset=long", flush=True)
+    case = inputs.preset_case("long", seed=0)
+    t, kc, vc = _fp8_case(case, KS_LONG, VS_LONG)
+    _write(t, KS_LONG, VS_LONG)
+    okc, ovc = _oracle_pools(case, kc, vc, KS_LONG, VS_LONG)
+    want = oracle.decode(case.query, okc, ovc, case.block_tables, case.context_lens,
+                         case.block_size, case.scale, KS_LONG, VS_LONG)
+    P = G.bench_partitions()[1]["long"]
+    got_p, po, pm, ps = _partitioned(t, case, P, ks=KS_LONG, vs=VS_LONG)
+    assert G.max_err(G.host(got_p), want) <= G.BF16_TOL
+    o_w, lse_w, n = oracle.decode_partitions(case.query, okc, ovc, case.block_tables,
+                                             case.context_lens, case.block_size, case.scale,
+                                             KS_LONG, VS_LONG, P)
+    G.check_records(po, pm, ps, o_w, lse_w, n)
+    assert G.max_err(G.host(_decode(t, case, ks=KS_LONG, vs=VS_LONG)), want) <= G.BF16_TOL
 
 
 def test_bf16_output_fp8():

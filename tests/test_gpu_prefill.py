@@ -38,7 +38,13 @@ def test_small_prefill_cases(existing, chunks, hq, hkv, d, bs):
     assert G.max_err(G.host(_run(case, t)), want) <= G.BF16_TOL
 
 
-def test_prefill_full_size_sampled_rows():
+def test_prefill_full_size_strided_rows():
+    """The chunked-prefill batch the benchmark times (16 sequences, 0..6000
+    cached tokens, 512-token chunks), checked on every 16th query position
+    of every sequence (the residue changes with the sequence, so every row
+    block of 256 (position, head) rows and the causal diagonal of every key
+    tile are reached) plus the first and last two positions of each chunk,
+    all 24 heads each, against the oracle; every output is finite."""
     print("[prefill] preset=prefill", flush=True)
     case = inputs.preset_case("prefill", seed=0)
     t = G.to_dev(case)
@@ -47,13 +53,12 @@ def test_prefill_full_size_sampled_rows():
     kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
                                 case.slot_mapping, case.block_size)
     qsl = case.query_start_loc
-    seqs = [int(np.argmax(case.context_lens)), int(np.argmin(case.context_lens)), 5]
     rows = set()
-    for s in seqs:
+    for s in range(len(qsl) - 1):
         lo, hi = int(qsl[s]), int(qsl[s + 1])
-        rows |= {lo, lo + 1, lo + 63, lo + 64, lo + 255, hi - 2, hi - 1}
+        rows |= set(range(lo + s % 16, hi, 16)) | {lo, lo + 1, hi - 2, hi - 1}
     want = oracle.prefill(case.query, kc, vc, case.block_tables, qsl, case.context_lens,
-                          case.block_size, case.scale, seqs=seqs, rows=rows)
+                          case.block_size, case.scale, rows=rows)
     idx = sorted(rows)
     assert G.max_err(got[idx], want[idx]) <= G.BF16_TOL
     assert np.isfinite(got).all()
