@@ -88,7 +88,15 @@ def bench_partitions():
     return bench.DEFAULT_PARTITION, bench.FP8_DEFAULT_PARTITION
 
 
-def check_records(po, pm, ps, o_want, lse_want, num_parts, tol=BF16_TOL, lse_tol=1e-3):
+# lse_p bound: the matrix-core kernels round each softmax weight to BF16 (the
+# P operand of P.V) and sum the rounded weights, so l_p is within a relative
+# 2^-8 of the exact sum and ln l_p within ln(1 + 2^-8) = 3.9e-3; fp32
+# accumulation adds far less. o_p divides by the same rounded sum, so it
+# stays within the 2e-2 output bar.
+LSE_TOL = 4e-3
+
+
+def check_records(po, pm, ps, o_want, lse_want, num_parts, tol=BF16_TOL, lse_tol=LSE_TOL):
     """Every partition record of every (sequence, query head): lse_p = m_p +
     ln l_p and o_p against the oracle's (m_p and l_p alone are not unique)."""
     po, pm, ps = host(po), host(pm), host(ps)
@@ -97,7 +105,8 @@ def check_records(po, pm, ps, o_want, lse_want, num_parts, tol=BF16_TOL, lse_tol
             continue
         lse_g = pm[s, :, :k] + np.log(ps[s, :, :k])
         assert np.isfinite(lse_g).all(), s
-        assert np.abs(lse_g - lse_want[s, :, :k]).max() <= lse_tol, s
+        err = np.abs(lse_g - lse_want[s, :, :k]).max()
+        assert err <= lse_tol, (s, err)
         assert max_err(po[s, :, :k], o_want[s, :, :k]) <= tol, s
 
 
