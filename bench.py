@@ -56,9 +56,9 @@ _TILED_SRC = [os.path.join(_CSRC, f) for f in ("decode_tiled.hip", "pa_device.h"
 _FP8_SRC = [os.path.join(_CSRC, f) for f in ("decode_fp8.hip", "pa_device.h",
                                              "persistent_plan.h")]
 TRAFFIC_RECORDS = {
-    ("bf16", "mixed"): ("decode_mfma_mixed_64seq_hbm_counters.md", _DECODE_SRC),
-    ("bf16", "long"): ("decode_mfma_long_4seq_hbm_counters.md", _DECODE_SRC),
-    ("bf16", "uniform"): ("decode_tiled_uniform_8x2048_hbm_counters.md", _TILED_SRC),
+    ("bf16-split", "mixed"): ("decode_mfma_mixed_64seq_hbm_counters.md", _DECODE_SRC),
+    ("bf16-split", "long"): ("decode_mfma_long_4seq_hbm_counters.md", _DECODE_SRC),
+    ("bf16-split", "uniform"): ("decode_tiled_uniform_8x2048_hbm_counters.md", _TILED_SRC),
     ("fp8", "mixed"): ("decode_fp8_mixed_64seq_16layer.md", _FP8_SRC),
     ("fp8", "long"): ("decode_fp8_long_4seq_hbm_counters.md", _FP8_SRC),
 }
@@ -103,6 +103,10 @@ def parse():
     ap.add_argument("--fp8-partition-size", type=int, default=None,
                     help="partition size of the FP8 leg (default: 2048 for the mixed workload, "
                          "512 for the long one, 256 for the uniform one)")
+    ap.add_argument("--mode", default=None, choices=["split", "balanced", "single", "whole"],
+                    help="how the step runs attention: split (pa_decode_partitioned + "
+                         "pa_reduce, the default), balanced (pa_decode_partitioned_balanced + "
+                         "pa_reduce), single (pa_decode_balanced) or whole (pa_decode)")
     ap.add_argument("--side-decode", type=int, default=1,
                     help="with the mixed workload, also time the long-context and uniform "
                          "decode workloads (0: skip)")
@@ -579,7 +583,22 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     }
 
 
-def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None):
+# How a decode step runs the attention:
+#  "split"    pa_decode_partitioned + pa_reduce (whole units per workgroup)
+#  "balanced" pa_decode_partitioned_balanced + pa_reduce (equal shares per
+#             compute unit; cut units merged by the call's second kernel)
+#  "single"   pa_decode_balanced (single pass, equal shares; no reduce)
+#  "whole"    pa_decode (single pass, one (sequence, KV head) per workgroup)
+# The split path is the fastest measured on every decode workload here
+# (mixed 71.5 us against 82.9 balanced and 84.7 single; long 63.1 against
+# 71.2 and 79.8; uniform 16.2 against 27.4 single): with the memory system
+# saturated, a piece end costs more than the round that balancing saves.
+DEFAULT_MODE = {"mixed": "split", "long": "split", "uniform": "split"}
+MODE_KERNEL = {"split": "pa_decode_partitioned", "balanced": "pa_decode_partitioned_balanced",
+               "single": "pa_decode_balanced", "whole": "pa_decode"}
+
+
+def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
     """One decode workload at full size: K timed steps (per pool set: the
     slot write of the step's new K/V, pa_decode_partitioned at partition
     size P, pa_reduce) after W warm-up steps, then the decode kernel's own
@@ -608,17 +627,31 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None):
     scale = meta["scale"]
     stream = torch.cuda.current_stream()
 
+    scratch = pa.decode_scratch(dev)
+
     def decode(li):
         L = layers[li]
-        pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
-                                 bt, cl, scale, P, stream=stream)
+        if mode == "single":
+            pa.pa_decode_balanced(outs[li], L["query"], L["key_cache"], L["value_cache"], bt, cl,
+                                  scale, scratch, stream=stream)
+        elif mode == "whole":
+            pa.pa_decode(outs[li], L["query"], L["key_cache"], L["value_cache"], bt, cl, scale,
+                         stream=stream)
+        elif mode == "balanced":
+            pa.pa_decode_partitioned_balanced(po, pm, ps, L["query"], L["key_cache"],
+                                              L["value_cache"], bt, cl, scale, P, scratch,
+                                              stream=stream)
+        else:
+            pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
+                                     bt, cl, scale, P, stream=stream)
 
     def step():
         for li, L in enumerate(layers):
             pa.pa_reshape_and_cache(L["key"], L["value"], L["key_cache"], L["value_cache"], sm,
                                     stream=stream)
             decode(li)
-            pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
+            if mode in ("split", "balanced"):
+                pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -646,21 +679,24 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None):
         "tokens_per_s": round(S * (layers_n // pre.get("layers", 1)) / (ms_step * 1e-3), 1),
         "kv_gbs_effective": round(gbs, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "mode": mode,
         "config": {"num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
                    "context_len_range": [int(lens.min()), int(lens.max())],
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": pre["block_size"], "pool_blocks": int(meta["num_blocks"]),
                    "layers": pre.get("layers", 1), "pool_sets_per_step": layers_n,
-                   "partition_size": P, "seed": seed},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned",
+                   "partition_size": P if mode in ("split", "balanced") else None,
+                   "seed": seed},
+        "roofline": {"bound": "hbm", "kernel": MODE_KERNEL[mode],
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": decode_traffic("bf16", W, P, seed),
+                     "traffic": decode_traffic("bf16-" + mode, W,
+                                               P if mode in ("split", "balanced") else None, seed),
                      "avg_launch_us": round(kern_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
     if fp8_P:
-        del po, pm, ps, outs
+        del po, pm, ps, outs, scratch
         res["fp8"] = fp8_leg(layers, meta, fp8_P, steps, warmup, dev, W, seed)
     del layers
     torch.cuda.empty_cache()
@@ -680,7 +716,8 @@ def main():
     W = args.workload
     P = args.partition_size or DEFAULT_PARTITION[W]
     fp8_P = (args.fp8_partition_size or FP8_DEFAULT_PARTITION[W]) if args.fp8 else None
-    main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P)
+    mode = args.mode or DEFAULT_MODE[W]
+    main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P, mode)
 
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
@@ -695,7 +732,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), rounded to BF16)",
-        "config": {"workload": main_leg["workload"], **main_leg["config"]},
+        "config": {"workload": main_leg["workload"], "mode": main_leg["mode"],
+                   **main_leg["config"]},
         "tokens_per_s": main_leg["tokens_per_s"],
         "pct_of_hbm_peak": main_leg["pct_of_hbm_peak"],
         "roofline": main_leg["roofline"],
@@ -709,7 +747,7 @@ def main():
         for w2 in ("long", "uniform"):
             f2 = FP8_DEFAULT_PARTITION[w2] if (args.fp8 and w2 == "long") else None
             result[w2] = decode_leg(w2, DEFAULT_PARTITION[w2], args.steps, args.warmup, dev,
-                                    args.seed, f2)
+                                    args.seed, f2, DEFAULT_MODE[w2])
     if args.prefill_reps > 0:
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)

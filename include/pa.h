@@ -249,6 +249,53 @@ pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
                     int32_t max_parts, pa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Balanced decode: the same operations as pa_decode and
+ * pa_decode_partitioned (same arguments, outputs and error behaviour), with
+ * the batch's work cut into equal shares, one per compute unit, whatever the
+ * mix of context lengths ([P2] s.3: a continuous batch mixes short and long
+ * requests). Work is counted in rounds of 128 tokens of one KV head; a
+ * unit (one output record: a (sequence, KV head), or a (sequence, KV head,
+ * partition)) that straddles two shares is computed in pieces whose softmax
+ * states (running max, sum, unnormalised output) go to `scratch`; a second,
+ * small kernel launched by the same call merges each such unit's pieces in a
+ * fixed order with the log-sum-exp rule of pa_reduce and writes its record.
+ * Results are deterministic and do not depend on physical block ids. In
+ * single-pass mode no separate reduce is needed.
+ *
+ *  scratch        [device] caller-owned, 16-byte aligned, at least
+ *                 pa_decode_scratch_bytes() bytes; no initial contents are
+ *                 needed (every byte the merge reads is written earlier in
+ *                 the same call). One buffer serves any number of calls
+ *                 issued in order on one stream; calls that may run at the
+ *                 same time (other streams) must not share one.
+ *  scratch_bytes  its size in bytes (PA_EINVAL when smaller than needed).
+ * Covered on the matrix cores: BF16 pools, head_dim 256, block_size a
+ * multiple of 16, num_seqs <= 1024, query heads per KV head <= 8, partition
+ * sizes that are multiples of 16; other supported shapes run the kernels of
+ * pa_decode / pa_decode_partitioned and leave scratch untouched.
+ */
+size_t pa_decode_scratch_bytes(void); /* for the current device: a 16-byte
+                                         merge entry and two piece slots of
+                                         8,320 bytes per compute unit */
+pa_status pa_decode_balanced(void *out, const void *query, const void *key_cache,
+                             const void *value_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                             pa_dtype kv_dtype, pa_dtype out_dtype, void *scratch,
+                             size_t scratch_bytes, hipStream_t stream);
+pa_status pa_decode_partitioned_balanced(float *part_out, float *part_max, float *part_sum,
+                                         const void *query, const void *key_cache,
+                                         const void *value_cache, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int32_t num_blocks,
+                                         float scale, int32_t partition_size, int32_t max_parts,
+                                         pa_dtype kv_dtype, void *scratch, size_t scratch_bytes,
+                                         hipStream_t stream);
+
+/*
  * pa_prefill_chunk - chunked paged prefill ([P2] s.4 chunked prefill; [P4]
  * "FlashAttention-2 Integration": causal attention over packed, unpadded
  * queries). The chunk's own K/V must already be in the pools

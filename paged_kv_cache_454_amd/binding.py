@@ -237,6 +237,67 @@ def pa_decode_partitioned(part_out, part_max, part_sum, query, key_cache, value_
         _stream(stream)))
 
 
+def pa_decode_scratch_bytes():
+    """Scratch bytes a balanced decode call needs on the current device."""
+    return int(lib().pa_decode_scratch_bytes())
+
+
+def decode_scratch(device=None):
+    """A scratch buffer for the balanced decode calls (no initial contents
+    needed; one buffer serves any number of calls issued in order on one
+    stream)."""
+    return torch.empty(pa_decode_scratch_bytes(), dtype=torch.uint8,
+                       device=device if device is not None else torch.cuda.current_device())
+
+
+def _scratch(scratch):
+    return _dev(scratch, "scratch", torch.uint8, 1), scratch.numel()
+
+
+def pa_decode_balanced(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                       scratch, stream=None):
+    """Single-pass paged decode with every workgroup given an equal share of
+    the batch; out [num_seqs][H_q][d]. scratch: decode_scratch()."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    if query.shape[0] != num_seqs or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("query/out must be [num_seqs][num_q_heads][head_dim]")
+    hq = query.shape[1]
+    sp, sn = _scratch(scratch)
+    check(lib().pa_decode_balanced(_dev(out, "out"), _dev(query, "query"),
+                                   _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                                   block_tables.data_ptr(), context_lens.data_ptr(), num_seqs, hq,
+                                   hkv, d, bs, block_tables.shape[1], num_blocks, float(scale),
+                                   _dtype(key_cache, "pools"), _dtype(out, "out"), sp, sn,
+                                   _stream(stream)))
+
+
+def pa_decode_partitioned_balanced(part_out, part_max, part_sum, query, key_cache, value_cache,
+                                   block_tables, context_lens, scale, partition_size, scratch,
+                                   stream=None):
+    """pa_decode_partitioned with every workgroup given an equal share of the
+    batch (same records). scratch: decode_scratch()."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    hq = query.shape[1]
+    if query.shape[0] != num_seqs:
+        raise ValueError("query must be [num_seqs][num_q_heads][head_dim]")
+    if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (num_seqs, hq) or part_out.shape[3] != d:
+        raise ValueError("part_out must be float32 [num_seqs][num_q_heads][max_parts][head_dim]")
+    max_parts = part_out.shape[2]
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (num_seqs, hq, max_parts):
+            raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
+    sp, sn = _scratch(scratch)
+    check(lib().pa_decode_partitioned_balanced(
+        _dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
+        _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
+        float(scale), int(partition_size), max_parts, _dtype(key_cache, "pools"), sp, sn,
+        _stream(stream)))
+
+
 def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                   k_scale, v_scale, stream=None):
     """pa_decode over FP8 pools (codes times k_scale / v_scale); bfloat16 query."""

@@ -1,6 +1,7 @@
 // Internal launchers called by the C entry points after argument checks.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pa_internal.h"
@@ -58,7 +59,33 @@ struct DecodeParams {
   int32_t kv_fp8;   // E4M3FN code pools, BF16 queries; logits scale by k_scale,
   float k_scale;    // outputs by v_scale (used only when kv_fp8)
   float v_scale;
+  void *scratch;          // balanced kernels: merge entries + piece slots
+  int64_t scratch_bytes;
 };
+
+// Balanced decode (every workgroup an equal share of the rounds). A unit
+// that crosses workgroup boundaries is computed in pieces; each piece's
+// softmax state goes to a scratch slot, and a second, small kernel merges
+// the pieces of every such unit. Scratch layout: one merge entry per
+// workgroup, int4 (sequence, KV head, partition, piece count; count 0 = no
+// unit to merge) - written by the decode kernel for the cut unit that
+// starts in that workgroup - padded to 256 bytes; then two piece slots per
+// workgroup of BAL_SLOT_FLOATS floats: the unnormalised output
+// [BAL_GMAX][256], the running maxima [BAL_GMAX] (log2 domain), the sums
+// [BAL_GMAX], a poison flag, padding. Every byte the merge reads was
+// written by the decode launch before it, so scratch needs no initial
+// contents.
+constexpr int BAL_MAX_SEQS = 1024;
+constexpr int BAL_GMAX = 8;
+constexpr int BAL_SLOT_FLOATS = BAL_GMAX * 256 + 4 * BAL_GMAX;
+__host__ __device__ inline int64_t bal_entry_bytes(int grid) {
+  return ((int64_t)grid * 16 + 255) & ~(int64_t)255;
+}
+int64_t bal_scratch_bytes(int grid);
+// Scratch bytes the balanced kernels need on the current device.
+int64_t bal_scratch_bytes_current();
+// False when the shape is not covered (the caller then uses launch_decode).
+bool launch_decode_balanced(const DecodeParams &p, hipStream_t stream);
 
 pa_status launch_decode(const DecodeParams &p, hipStream_t stream);
 

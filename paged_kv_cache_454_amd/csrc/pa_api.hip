@@ -384,6 +384,120 @@ extern "C" pa_status pa_decode_partitioned_fp8(
   return pa::launch_decode(p, stream);
 }
 
+// Checks of a balanced call's scratch (caller-owned device memory, zero
+// before the first call; the kernels leave the counters at zero).
+static pa_status check_scratch(const char *fn, const void *scratch, size_t scratch_bytes) {
+  const int64_t need = pa::bal_scratch_bytes_current();
+  if (!scratch) return pa::fail(PA_EINVAL, "%s: scratch is NULL", fn);
+  if ((int64_t)scratch_bytes < need)
+    return pa::fail(PA_EINVAL, "%s: scratch_bytes=%zu < %lld (pa_decode_scratch_bytes)", fn,
+                    scratch_bytes, (long long)need);
+  if ((uintptr_t)scratch % 16 != 0)
+    return pa::fail(PA_EINVAL, "%s: scratch must be 16-byte aligned", fn);
+  return PA_OK;
+}
+
+extern "C" size_t pa_decode_scratch_bytes(void) {
+  return (size_t)pa::bal_scratch_bytes_current();
+}
+
+extern "C" pa_status pa_decode_balanced(void *out, const void *query, const void *key_cache,
+                                        const void *value_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        float scale, pa_dtype kv_dtype, pa_dtype out_dtype,
+                                        void *scratch, size_t scratch_bytes,
+                                        hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_balanced";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  st = check_scratch(fn, scratch, scratch_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = 0;
+  p.max_parts = 1;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.scratch = scratch;
+  p.scratch_bytes = (int64_t)scratch_bytes;
+  if (pa::launch_decode_balanced(p, stream)) return pa::check_launch("decode");
+  p.scratch = nullptr;  // a shape the balanced kernel does not cover
+  return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_decode_partitioned_balanced(
+    float *part_out, float *part_max, float *part_sum, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+    int32_t partition_size, int32_t max_parts, pa_dtype kv_dtype, void *scratch,
+    size_t scratch_bytes, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_partitioned_balanced";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size % block_size != 0)
+    return pa::fail(PA_EINVAL, "%s: partition_size=%d must be >= 16 and a multiple of block_size=%d",
+                    fn, partition_size, block_size);
+  if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
+  st = check_scratch(fn, scratch, scratch_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!part_out || !part_max || !part_sum || !query || !key_cache || !value_cache ||
+      !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = partition_size;
+  p.max_parts = max_parts;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.scratch = scratch;
+  p.scratch_bytes = (int64_t)scratch_bytes;
+  if (pa::launch_decode_balanced(p, stream)) return pa::check_launch("decode");
+  p.scratch = nullptr;
+  return pa::launch_decode(p, stream);
+}
+
 extern "C" pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
                                const float *part_sum, const int32_t *context_lens,
                                int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
