@@ -284,6 +284,26 @@ pa_status pa_decode_balanced(void *out, const void *query, const void *key_cache
                              int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
                              pa_dtype kv_dtype, pa_dtype out_dtype, void *scratch,
                              size_t scratch_bytes, hipStream_t stream);
+/*
+ * pa_decode_balanced_static - pa_decode_balanced for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without
+ * scratch, the same results. Its scratch is a static array inside the
+ * library, 8 MiB per GPU it runs on, held until the process ends; no call
+ * allocates or frees anything. Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (other streams) race;
+ * nothing in it needs to start at zero. PA_EUNSUPPORTED when the device
+ * would need more than 8 MiB (pa_decode_scratch_bytes() above it, i.e. more
+ * than 503 compute units); PA_EHIP when the array's device address cannot
+ * be obtained.
+ */
+pa_status pa_decode_balanced_static(void *out, const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, float scale, pa_dtype kv_dtype,
+                                    pa_dtype out_dtype, hipStream_t stream);
 pa_status pa_decode_partitioned_balanced(float *part_out, float *part_max, float *part_sum,
                                          const void *query, const void *key_cache,
                                          const void *value_cache, const int32_t *block_tables,

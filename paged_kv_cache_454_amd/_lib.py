@@ -42,6 +42,8 @@ SIGNATURES = {
     "pa_decode_scratch_bytes": (ctypes.c_size_t, []),
     "pa_decode_balanced": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _f32, _st, _st, _p, ctypes.c_size_t, _p]),
+    "pa_decode_balanced_static": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _f32, _st, _st, _p]),
     "pa_decode_partitioned_balanced": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _f32, _i32, _i32, _st, _p,
                                              ctypes.c_size_t, _p]),

@@ -272,6 +272,22 @@ def pa_decode_balanced(out, query, key_cache, value_cache, block_tables, context
                                    _stream(stream)))
 
 
+def pa_decode_balanced_static(out, query, key_cache, value_cache, block_tables, context_lens,
+                              scale, stream=None):
+    """pa_decode_balanced with the library's static scratch: allocates
+    nothing (calls that overlap in time on one GPU race)."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    if query.shape[0] != num_seqs or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("query/out must be [num_seqs][num_q_heads][head_dim]")
+    hq = query.shape[1]
+    check(lib().pa_decode_balanced_static(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), block_tables.data_ptr(), context_lens.data_ptr(),
+        num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks, float(scale),
+        _dtype(key_cache, "pools"), _dtype(out, "out"), _stream(stream)))
+
+
 def pa_decode_partitioned_balanced(part_out, part_max, part_sum, query, key_cache, value_cache,
                                    block_tables, context_lens, scale, partition_size, scratch,
                                    stream=None):

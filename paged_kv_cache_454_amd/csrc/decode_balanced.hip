@@ -40,6 +40,8 @@
 // kernel; see decode_mfma.hip for the lane layouts.
 #include <math.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "pa_device.h"
 #include "persistent_plan.h"
@@ -770,6 +772,43 @@ int64_t bal_scratch_bytes(int grid) {
 }
 
 int64_t bal_scratch_bytes_current() { return bal_scratch_bytes(persist::num_cus()); }
+
+// Scratch for pa_decode_balanced_static, for callers that cannot allocate:
+// one array per GPU the library runs on, held until the process ends, shared
+// by every call on that GPU (calls that overlap in time race; nothing in it
+// needs to start at zero). Host code never uses the array's name as an
+// address: its device address is looked up once per device.
+constexpr int64_t kStaticScratchBytes = 8 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_static_mu;
+void *g_static_ptr[64] = {nullptr};
+}  // namespace
+
+int64_t bal_static_scratch_limit() { return kStaticScratchBytes; }
+
+// The current device's copy of the static scratch (looked up on the first
+// call with that device current); null with a message on failure.
+void *bal_static_scratch(const char **why) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    *why = "no current HIP device (or device index >= 64)";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      *why = "hipGetSymbolAddress of the static scratch failed";
+      return nullptr;
+    }
+    g_static_ptr[dev] = ptr;
+  }
+  return g_static_ptr[dev];
+}
 
 // Launch the balanced matrix-core kernel when the shape is one it covers
 // and p.scratch holds bal_scratch_bytes(#CUs); false otherwise.

@@ -84,6 +84,10 @@ __host__ __device__ inline int64_t bal_entry_bytes(int grid) {
 int64_t bal_scratch_bytes(int grid);
 // Scratch bytes the balanced kernels need on the current device.
 int64_t bal_scratch_bytes_current();
+// The static scratch of pa_decode_balanced_static on the current device
+// (null, with *why set, when its address cannot be obtained), and its size.
+void *bal_static_scratch(const char **why);
+int64_t bal_static_scratch_limit();
 // False when the shape is not covered (the caller then uses launch_decode).
 bool launch_decode_balanced(const DecodeParams &p, hipStream_t stream);
 

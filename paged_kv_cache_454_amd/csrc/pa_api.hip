@@ -448,6 +448,59 @@ extern "C" pa_status pa_decode_balanced(void *out, const void *query, const void
   return pa::launch_decode(p, stream);
 }
 
+extern "C" pa_status pa_decode_balanced_static(void *out, const void *query,
+                                               const void *key_cache, const void *value_cache,
+                                               const int32_t *block_tables,
+                                               const int32_t *context_lens, int32_t num_seqs,
+                                               int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size,
+                                               int32_t max_blocks_per_seq, int32_t num_blocks,
+                                               float scale, pa_dtype kv_dtype,
+                                               pa_dtype out_dtype, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_balanced_static";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  const int64_t need = pa::bal_scratch_bytes_current();
+  if (need > pa::bal_static_scratch_limit())
+    return pa::fail(PA_EUNSUPPORTED,
+                    "%s: this device needs %lld bytes of scratch, more than the static %lld", fn,
+                    (long long)need, (long long)pa::bal_static_scratch_limit());
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  const char *why = "";
+  void *scratch = pa::bal_static_scratch(&why);
+  if (!scratch) return pa::fail(PA_EHIP, "%s: %s", fn, why);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = 0;
+  p.max_parts = 1;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.out_bf16 = out_dtype == PA_BF16;
+  p.scratch = scratch;
+  p.scratch_bytes = pa::bal_static_scratch_limit();
+  if (pa::launch_decode_balanced(p, stream)) return pa::check_launch("decode");
+  p.scratch = nullptr;  // a shape the balanced kernel does not cover
+  return pa::launch_decode(p, stream);
+}
+
 extern "C" pa_status pa_decode_partitioned_balanced(
     float *part_out, float *part_max, float *part_sum, const void *query, const void *key_cache,
     const void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
