@@ -46,6 +46,7 @@ constexpr int STAGES = 4;               // K/V tiles in the LDS ring (3 in fligh
 constexpr int PAIR = 1040;              // bytes per token pair in LDS: 2 x 512 + 16 of bank offset
 constexpr int TILE_BYTES = (KT / 2) * PAIR;  // one K (or V) tile
 constexpr int MAX_TABLE = 2048;         // block ids staged in LDS
+constexpr int NXCD = 8;                 // XCDs (dies) the workgroups are dealt to
 constexpr float kLazy = 8.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -160,9 +161,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int half = lane >> 5;  // which 8 of a 16-wide k step this lane supplies
   const int l32 = lane & 31;
 
-  // Later row blocks see more tokens: launch them first.
-  const int rb = row_blocks - 1 - (int)(blockIdx.x % row_blocks);
-  const int sk = blockIdx.x / row_blocks;
+  // Workgroup id -> (sequence, KV head, row block). Ids are dealt to the 8
+  // XCDs round-robin (id % 8), and each XCD has its own L2: the (sequence,
+  // KV head) pairs are dealt to the XCDs and each keeps all its row blocks on
+  // its XCD, so they read the sequence's K/V through one L2. Later row
+  // blocks see more tokens: launch them first.
+  const int SK = p.num_seqs * p.num_kv_heads;
+  const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
+  const int sk = xcd + NXCD * (slot / row_blocks);
+  if (sk >= SK) return;
+  const int rb = row_blocks - 1 - slot % row_blocks;
   const int kvh = sk % p.num_kv_heads;
   const int s = sk / p.num_kv_heads;
 
@@ -184,6 +192,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int last_row = min(rb * ROWS + ROWS, nrows) - 1;
   const int wg_limit = bad ? 0 : ctx0 + last_row / G + 1;
   const int ntiles = (wg_limit + KT - 1) / KT;
+  // Tiles that every row of this wave sees entirely need no mask.
+  const int wave_first_row = min(rb * ROWS + wave * 32, nrows - 1);
+  const int wave_min_lim = bad ? 0 : ctx0 + wave_first_row / G + 1;
 
   // Block ids of the tokens the workgroup reads, and the first invalid one:
   // a row that would read it gets NaN outputs (its reads become zeros).
@@ -306,11 +317,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4.
     float z[16];
     float mx = -INFINITY;
+    const bool full = t0 + KT <= wave_min_lim;  // uniform: no token of the tile is masked
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int tok = t0 + tok_of(8 * (e >> 2) + 4 * half + (e & 3));
       const float v = s0[e] * sl2;
-      z[e] = tok < limit ? v : -INFINITY;
+      if (full) {
+        z[e] = v;
+      } else {
+        const int tok = t0 + tok_of(8 * (e >> 2) + 4 * half + (e & 3));
+        z[e] = tok < limit ? v : -INFINITY;
+      }
       mx = fmaxf(mx, z[e]);
     }
     mx = other_half_max(mx);
@@ -404,7 +420,8 @@ bool launch_prefill_mfma(const PrefillParams &p, hipStream_t stream) {
   if (p.head_dim != D || p.block_size % 2 != 0 || p.max_blocks_per_seq > MAX_TABLE) return false;
   const int group = p.num_q_heads / p.num_kv_heads;
   const int64_t row_blocks = ((int64_t)p.max_query_len * group + ROWS - 1) / ROWS;
-  const int64_t grid = row_blocks * p.num_seqs * p.num_kv_heads;
+  const int64_t sk = (int64_t)p.num_seqs * p.num_kv_heads;
+  const int64_t grid = NXCD * row_blocks * ((sk + NXCD - 1) / NXCD);
   if (grid <= 0 || grid > 0x7fffffff) return false;
   switch (group) {
 #define PA_CASE(g)                                                                  \
