@@ -39,6 +39,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -107,6 +108,12 @@ def parse():
                     help="how the step runs attention: split (pa_decode_partitioned + "
                          "pa_reduce, the default), balanced (pa_decode_partitioned_balanced + "
                          "pa_reduce), single (pa_decode_balanced) or whole (pa_decode)")
+    ap.add_argument("--step", default=None, choices=["fused", "calls"],
+                    help="fused: each layer's step is one pa_decode_step call (the step's K/V "
+                         "write inside the decode and merge launches); calls: "
+                         "pa_reshape_and_cache, then the decode and pa_reduce (default: per "
+                         "workload, the faster measured). Split and whole modes only; the other "
+                         "form is timed too, as ms_per_step_other")
     ap.add_argument("--side-decode", type=int, default=1,
                     help="with the mixed workload, also time the long-context and uniform "
                          "decode workloads (0: skip)")
@@ -594,15 +601,23 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
 # 71.2 and 79.8; uniform 16.2 against 27.4 single): with the memory system
 # saturated, a piece end costs more than the round that balancing saves.
 DEFAULT_MODE = {"mixed": "split", "long": "split", "uniform": "split"}
-MODE_KERNEL = {"split": "pa_decode_partitioned", "balanced": "pa_decode_partitioned_balanced",
+MODE_KERNEL = {"split": "pa_decode_partitioned_planned",
+               "balanced": "pa_decode_partitioned_balanced",
                "single": "pa_decode_balanced", "whole": "pa_decode"}
+# Step form: one pa_decode_step call per layer, or the write, the decode and
+# the merge as three calls. Timed alternately in one run (median of three
+# each): mixed 1.2183 ms fused against 1.2447 ms, long 0.2120 against 0.2170,
+# uniform 0.1798 against 0.1799 (there the tiled kernel reads the step's
+# token from the pool, so both forms launch the same three kernels).
+DEFAULT_STEP = {"mixed": "fused", "long": "fused", "uniform": "fused"}
 
 
-def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
+def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_form="fused"):
     """One decode workload at full size: K timed steps (per pool set: the
     slot write of the step's new K/V, pa_decode_partitioned at partition
-    size P, pa_reduce) after W warm-up steps, then the decode kernel's own
-    launches timed back to back on the launch stream. Pool sets are the
+    size P, pa_reduce; as one pa_decode_step call when step_form is "fused")
+    after W warm-up steps, then the decode kernel's own launches timed back
+    to back on the launch stream. Pool sets are the
     mixed batch's 16 layers, or independent copies of a one-layer workload
     decoded in turn so that no step re-reads K/V the last one left in the
     caches. Returns the leg's figures (and the FP8 leg's, given fp8_P)."""
@@ -628,9 +643,19 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
     stream = torch.cuda.current_stream()
 
     scratch = pa.decode_scratch(dev)
+    # Plan buffers: the layers (pool sets) of a step share context lengths
+    # and block tables, so the first launch of a step plans and the others
+    # read its plan. Each step takes a new epoch (the lengths and tables of a
+    # real step change every step), so every step plans once. plan_step
+    # serves the fused step, plan_dec the planned partitioned decode.
+    plan_step = pa.decode_plan_buffer(dev)
+    plan_dec = pa.decode_plan_buffer(dev)
+    epoch = [0]
 
     def decode(li):
         L = layers[li]
+        if li == 0:
+            epoch[0] += 1
         if mode == "single":
             pa.pa_decode_balanced(outs[li], L["query"], L["key_cache"], L["value_cache"], bt, cl,
                                   scale, scratch, stream=stream)
@@ -642,10 +667,11 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
                                               L["value_cache"], bt, cl, scale, P, scratch,
                                               stream=stream)
         else:
-            pa.pa_decode_partitioned(po, pm, ps, L["query"], L["key_cache"], L["value_cache"],
-                                     bt, cl, scale, P, stream=stream)
+            pa.pa_decode_partitioned_planned(po, pm, ps, L["query"], L["key_cache"],
+                                             L["value_cache"], bt, cl, scale, P, plan_dec,
+                                             epoch[0], stream=stream)
 
-    def step():
+    def step_calls():
         for li, L in enumerate(layers):
             pa.pa_reshape_and_cache(L["key"], L["value"], L["key_cache"], L["value_cache"], sm,
                                     stream=stream)
@@ -653,17 +679,45 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
             if mode in ("split", "balanced"):
                 pa.pa_reduce(outs[li], po, pm, ps, cl, P, stream=stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for _ in range(steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / steps
+    def step_fused():
+        split = mode == "split"
+        epoch[0] += 1
+        for li, L in enumerate(layers):
+            pa.pa_decode_step(outs[li], L["query"], L["key"], L["value"], L["key_cache"],
+                              L["value_cache"], bt, cl, scale, P if split else 0,
+                              po if split else None, pm if split else None,
+                              ps if split else None, plan=plan_step, plan_epoch=epoch[0],
+                              stream=stream)
+
+    def time_steps(step):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for _ in range(steps):
+            step()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / steps
+
+    fusable = mode in ("split", "whole")
+    if not fusable:
+        step_form = "calls"
+    main = step_fused if step_form == "fused" else step_calls
+    other = step_calls if step_form == "fused" else step_fused
+    if fusable:
+        # The two forms alternate, three timings each, medians reported: the
+        # clocks settle over the first timings, so back-to-back single
+        # timings would favour whichever form runs second.
+        a, b = [], []
+        for _ in range(3):
+            a.append(time_steps(main))
+            b.append(time_steps(other))
+        ms_step, ms_other = statistics.median(a), statistics.median(b)
+    else:
+        ms_step, ms_other = time_steps(main), None
 
     # The decode kernel's own launches, timed in a separate pass (so the step
     # timing above carries no event overhead) on the stream they run on.
@@ -680,6 +734,8 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split"):
         "kv_gbs_effective": round(gbs, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "mode": mode,
+        "step": step_form,
+        "ms_per_step_other": round(ms_other, 5) if ms_other else None,
         "config": {"num_seqs": S, "context_tokens_per_layer": int(lens.sum()),
                    "context_len_range": [int(lens.min()), int(lens.max())],
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
@@ -717,7 +773,8 @@ def main():
     P = args.partition_size or DEFAULT_PARTITION[W]
     fp8_P = (args.fp8_partition_size or FP8_DEFAULT_PARTITION[W]) if args.fp8 else None
     mode = args.mode or DEFAULT_MODE[W]
-    main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P, mode)
+    main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P, mode,
+                          args.step or DEFAULT_STEP[W])
 
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
@@ -733,7 +790,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), rounded to BF16)",
         "config": {"workload": main_leg["workload"], "mode": main_leg["mode"],
-                   **main_leg["config"]},
+                   "step": main_leg["step"], **main_leg["config"]},
+        "ms_per_step_other": main_leg["ms_per_step_other"],
         "tokens_per_s": main_leg["tokens_per_s"],
         "pct_of_hbm_peak": main_leg["pct_of_hbm_peak"],
         "roofline": main_leg["roofline"],
@@ -747,7 +805,8 @@ def main():
         for w2 in ("long", "uniform"):
             f2 = FP8_DEFAULT_PARTITION[w2] if (args.fp8 and w2 == "long") else None
             result[w2] = decode_leg(w2, DEFAULT_PARTITION[w2], args.steps, args.warmup, dev,
-                                    args.seed, f2, DEFAULT_MODE[w2])
+                                    args.seed, f2, DEFAULT_MODE[w2],
+                                    args.step or DEFAULT_STEP[w2])
     if args.prefill_reps > 0:
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)

@@ -249,6 +249,97 @@ pa_status pa_reduce(void *out, const float *part_out, const float *part_max,
                     int32_t max_parts, pa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * pa_decode_step - one decode step of one layer in one call: the step's K/V
+ * rows join the cache and every sequence's query attends over its whole
+ * context, this step's token included ("vLLM Architecture, Memory and
+ * Benchmarks Deep Dive", s.1 and s.2; "Optimizing LLM Inference ...
+ * PagedAttention" (voronkin.com): blocks reached through the table appear
+ * contiguous to attention).
+ *
+ * The step's token of sequence s is position T_s - 1 (T_s = context_lens[s]
+ * counts it). Its rows key[s], value[s] are written to the slot its block
+ * table gives, table[s][(T_s - 1) / block_size] * block_size +
+ * (T_s - 1) % block_size; T_s = 0, T_s past the table's capacity or a block
+ * id outside the pool writes nothing (and decode then poisons that sequence's
+ * outputs as usual). The results equal pa_reshape_and_cache with those slots
+ * followed by pa_decode (partition_size == 0) or by pa_decode_partitioned and
+ * pa_reduce (partition_size > 0), within the same tolerance: the matrix-core
+ * kernel reads the step's token from key/value in a tile of its own, so its
+ * sums run in another order than the separate calls'.
+ *
+ * Where the matrix-core kernel covers the shape (BF16, head_dim 256, block
+ * size a multiple of 16, and in split mode more units than compute units
+ * with partitions of at least 256 tokens) this is two launches: the decode,
+ * then the merge (or, in single pass, the write) with the slot write inside
+ * it. Otherwise it is the write, the decode and the merge.
+ *
+ *  out            [device] out_dtype [num_seqs][num_q_heads][head_dim]
+ *  part_out, part_max, part_sum  [device] fp32 workspace as for
+ *                 pa_decode_partitioned (may be NULL when partition_size == 0)
+ *  query          [device] kv_dtype [num_seqs][num_q_heads][head_dim]
+ *  key, value     [device] kv_dtype [num_seqs][num_kv_heads][head_dim]: the
+ *                 step's rows (read only)
+ *  key_cache, value_cache  [device] pools as for pa_reshape_and_cache
+ *                 (written at the step's slots only)
+ *  block_tables, context_lens, sizes, scale  as pa_decode
+ *  partition_size 0 (single pass) or as pa_decode_partitioned; max_parts as
+ *                 there
+ *  kv_dtype       PA_F32 or PA_BF16
+ *  plan, plan_epoch  [device] NULL (each launch plans for itself), or a
+ *                 plan buffer and its epoch (see pa_decode_plan_bytes)
+ * Errors as pa_decode_partitioned and pa_reduce; every check is made before
+ * anything is launched, except that a failing later launch can leave the
+ * earlier ones queued.
+ */
+pa_status pa_decode_step(void *out, float *part_out, float *part_max, float *part_sum,
+                         const void *query, const void *key, const void *value, void *key_cache,
+                         void *value_cache, const int32_t *block_tables,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                         int32_t partition_size, int32_t max_parts, pa_dtype kv_dtype,
+                         pa_dtype out_dtype, void *plan, uint32_t plan_epoch,
+                         hipStream_t stream);
+
+/*
+ * Decode plans. The persistent matrix-core decode kernel starts by reading
+ * the context lengths, dealing the (sequence, KV head, partition) units to
+ * its workgroups and looking up each wave's first block ids: three dependent
+ * memory round trips before its first K/V load. Every layer of a decode step
+ * has the same lengths and tables ("vLLM Architecture, Memory and Benchmarks
+ * Deep Dive", s.2: one block table per sequence serves its whole cache), so
+ * the deal can be made once per step and read by each later layer's launch
+ * in one round trip.
+ *
+ * A plan buffer ([device], pa_decode_plan_bytes() bytes on the current
+ * device, any initial contents) is a cache of that deal, one slot per
+ * workgroup, each tagged with the launch that wrote it: entry point kind,
+ * grid, num_seqs, partition_size and the caller's plan_epoch. A launch given
+ * a buffer and an epoch reads its slot when the tag matches, and otherwise
+ * plans as usual and writes the slot. The caller's contract: one epoch value
+ * names one set of context_lens, block_tables and sizes (take a new epoch
+ * whenever they change, e.g. once per decode step); with a stale epoch the
+ * outputs are wrong (the kernel still never accesses memory outside the
+ * caller's buffers). Launches that share a buffer must run in order (one
+ * stream). Where the matrix-core kernel does not take the shape the buffer is
+ * not used. Results are bit for bit those of the calls without a plan.
+ */
+size_t pa_decode_plan_bytes(void);
+
+/* pa_decode_partitioned with a plan buffer and epoch (above): same
+ * arguments otherwise, results bit for bit equal to pa_decode_partitioned's. */
+pa_status pa_decode_partitioned_planned(float *part_out, float *part_max, float *part_sum,
+                                        const void *query, const void *key_cache,
+                                        const void *value_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        float scale, int32_t partition_size, int32_t max_parts,
+                                        pa_dtype kv_dtype, void *plan, uint32_t plan_epoch,
+                                        hipStream_t stream);
+
+/*
  * Balanced decode: the same operations as pa_decode and
  * pa_decode_partitioned (same arguments, outputs and error behaviour), with
  * the batch's work cut into equal shares, one per compute unit, whatever the

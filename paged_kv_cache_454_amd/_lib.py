@@ -18,6 +18,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_ENOMEM"
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
 _f32 = ctypes.c_float
 _st = ctypes.c_int
 
@@ -39,6 +40,12 @@ SIGNATURES = {
     "pa_decode_partitioned": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _f32, _i32, _i32, _st, _p]),
     "pa_reduce": (_st, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _st, _p]),
+    "pa_decode_step": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                             _i32, _i32, _i32, _f32, _i32, _i32, _st, _st, _p, _u32, _p]),
+    "pa_decode_plan_bytes": (ctypes.c_size_t, []),
+    "pa_decode_partitioned_planned": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _f32, _i32, _i32, _st, _p,
+                                            _u32, _p]),
     "pa_decode_scratch_bytes": (ctypes.c_size_t, []),
     "pa_decode_balanced": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _f32, _st, _st, _p, ctypes.c_size_t, _p]),

@@ -372,6 +372,87 @@ def pa_reduce(out, part_out, part_max, part_sum, context_lens, partition_size, s
                           int(partition_size), max_parts, _dtype(out, "out"), _stream(stream)))
 
 
+def pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables, context_lens,
+                   scale, partition_size=0, part_out=None, part_max=None, part_sum=None,
+                   plan=None, plan_epoch=0, stream=None):
+    """One decode step: key/value [num_seqs][H_KV][d] (the step's token, at
+    position context_lens[s] - 1) join the pools at the slot the block table
+    gives, then out [num_seqs][H_q][d] = attention over the whole context.
+    partition_size > 0 splits the context (part_* as for
+    pa_decode_partitioned); 0 is a single pass. plan: None or a
+    decode_plan_buffer(), with plan_epoch naming this step's lengths and
+    tables (a launch whose epoch matches reads the plan, otherwise writes it)."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    hq = query.shape[1]
+    if query.shape[0] != num_seqs or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("query/out must be [num_seqs][num_q_heads][head_dim]")
+    for t, nm in ((key, "key"), (value, "value")):
+        if tuple(t.shape) != (num_seqs, hkv, d) or t.dtype != key_cache.dtype:
+            raise ValueError(f"{nm} must be [num_seqs][num_kv_heads][head_dim] in the pools' dtype")
+    if partition_size:
+        if part_out is None or part_max is None or part_sum is None:
+            raise ValueError("a split step needs part_out, part_max and part_sum")
+        if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (num_seqs, hq) or \
+                part_out.shape[3] != d:
+            raise ValueError("part_out must be float32 [num_seqs][num_q_heads][max_parts][head_dim]")
+        max_parts = part_out.shape[2]
+        for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+            if tuple(t.shape) != (num_seqs, hq, max_parts):
+                raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
+        parts = [_dev(part_out, "part_out", torch.float32),
+                 _dev(part_max, "part_max", torch.float32),
+                 _dev(part_sum, "part_sum", torch.float32)]
+    else:
+        max_parts = 1
+        parts = [None, None, None]
+    check(lib().pa_decode_step(
+        _dev(out, "out"), *parts, _dev(query, "query"), _dev(key, "key"), _dev(value, "value"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
+        float(scale), int(partition_size), max_parts, _dtype(key_cache, "pools"),
+        _dtype(out, "out"), _plan(plan), int(plan_epoch) & 0xffffffff, _stream(stream)))
+
+
+def _plan(plan):
+    return None if plan is None else _dev(plan, "plan", torch.uint8, 1)
+
+
+def pa_decode_plan_bytes():
+    """Bytes of a decode plan buffer on the current device."""
+    return int(lib().pa_decode_plan_bytes())
+
+
+def decode_plan_buffer(device=None):
+    """A plan buffer for the planned decode calls (any initial contents)."""
+    return torch.empty(pa_decode_plan_bytes(), dtype=torch.uint8,
+                       device=device if device is not None else torch.cuda.current_device())
+
+
+def pa_decode_partitioned_planned(part_out, part_max, part_sum, query, key_cache, value_cache,
+                                  block_tables, context_lens, scale, partition_size, plan,
+                                  plan_epoch, stream=None):
+    """pa_decode_partitioned with a plan buffer and epoch (see pa_decode_step)."""
+    num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
+                                                    context_lens, "num_seqs")
+    hq = query.shape[1]
+    if query.shape[0] != num_seqs:
+        raise ValueError("query must be [num_seqs][num_q_heads][head_dim]")
+    if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (num_seqs, hq) or part_out.shape[3] != d:
+        raise ValueError("part_out must be float32 [num_seqs][num_q_heads][max_parts][head_dim]")
+    max_parts = part_out.shape[2]
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (num_seqs, hq, max_parts):
+            raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
+    check(lib().pa_decode_partitioned_planned(
+        _dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
+        _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
+        float(scale), int(partition_size), max_parts, _dtype(key_cache, "pools"), _plan(plan),
+        int(plan_epoch) & 0xffffffff, _stream(stream)))
+
+
 def pa_prefill_chunk(out, query, key_cache, value_cache, block_tables, query_start_loc,
                      context_lens, max_query_len, scale, stream=None):
     """Causal chunked prefill; query/out packed [num_q_tokens][H_q][d]."""

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-HIP_SOURCES = ["cache_write.hip", "copy_blocks.hip", "read_probe.hip", "decode.hip", "decode_tiled.hip", "decode_mfma.hip", "decode_balanced.hip", "decode_fp8.hip", "reduce.hip", "prefill.hip", "prefill_mfma.hip",
+HIP_SOURCES = ["cache_write.hip", "copy_blocks.hip", "read_probe.hip", "decode.hip", "decode_tiled.hip", "decode_mfma.hip", "decode_balanced.hip", "decode_fp8.hip", "reduce.hip", "append.hip", "prefill.hip", "prefill_mfma.hip",
                "pa_api.hip"]
 HOST_SOURCES = ["errors.cpp", "alloc.cpp"]
 

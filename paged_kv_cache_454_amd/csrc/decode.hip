@@ -299,6 +299,8 @@ pa_status launch_decode(const DecodeParams &p, hipStream_t stream) {
   if (grid > 0x7fffffff) return fail(PA_EUNSUPPORTED, "decode: grid of %lld workgroups", (long long)grid);
   if (launch_decode_fp8(p, stream)) return check_launch("decode");
   if (launch_decode_mfma(p, stream)) return check_launch("decode");
+  // Only the matrix-core kernel reads a step's token from new_key/new_value.
+  if (p.new_key) return fail(PA_EUNSUPPORTED, "decode: step rows need the matrix-core kernel");
   if (launch_decode_tiled(p, (unsigned)grid, stream)) return check_launch("decode");
   if (p.kv_fp8)
     launch_generic_d<fp8_t>(p, group, (unsigned)grid, stream);

@@ -164,7 +164,7 @@ void decode_fp8_kernel(DecodeParams p) {
   __shared__ int mg_bad[NW];
   __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
-  __shared__ int ubadpart[MAXU];   // part * 2 + bad
+  __shared__ int ubadpart[MAXU];   // part * 4 + 2 * append + bad (append unused here)
   __shared__ uint32_t act_lds[2];
 
   const int lane = threadIdx.x & 63;
@@ -527,7 +527,7 @@ void decode_fp8_kernel(DecodeParams p) {
     // All waves merge the unit's 8 partial states and store it (fixed store
     // count; stores that must not happen fall past num_records).
     const int64_t qrow = (int64_t)uj.x * HQ + (int64_t)uj.y * G;
-    const int part = __builtin_amdgcn_readfirstlane(ubadpart[j]) >> 1;
+    const int part = __builtin_amdgcn_readfirstlane(ubadpart[j]) >> 2;
     constexpr int ITER = (G * D + NW * 64 - 1) / (NW * 64);
 #pragma unroll 1
     for (int it = 0; it < ITER; ++it) {
@@ -575,7 +575,8 @@ void decode_fp8_kernel(DecodeParams p) {
 // Launch the FP8 matrix-core kernel when the shape is one it covers; false
 // otherwise (the caller then uses the generic kernel).
 bool launch_decode_fp8(const DecodeParams &p, hipStream_t stream) {
-  if (!p.kv_fp8 || p.head_dim != D || p.block_size % HALF != 0 || p.query_start_loc) return false;
+  if (!p.kv_fp8 || p.head_dim != D || p.block_size % HALF != 0 || p.query_start_loc || p.new_key)
+    return false;
   if (p.partition_size > 0 && p.partition_size % TILE != 0) return false;
   if ((int64_t)p.num_seqs * p.max_blocks_per_seq * 4 > 0x7fffffff) return false;
   if ((int64_t)p.block_size * D * p.num_kv_heads * p.num_blocks > ((int64_t)1 << 47)) return false;

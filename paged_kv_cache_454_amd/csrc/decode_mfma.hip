@@ -44,6 +44,12 @@
 //  * Rows past the context lie outside the loads' num_records and read as
 //    zeros; their logits are -inf. An out-of-pool block id gives an empty
 //    tile and poisons only that unit's outputs with NaN.
+//  * Decode step (new_key set): the last unit of each sequence streams its
+//    pool tokens up to T - 2 and then one more tile whose only row is the
+//    step's token, read from the step's K/V rows (same row layout, so the
+//    same loads; the other rows lie past num_records). Nothing this launch
+//    reads comes from that token's slot, so the slot write may run later on
+//    the stream (the merge kernel does it).
 #include <math.h>
 
 #include "launch.h"
@@ -138,9 +144,24 @@ struct DescM {
   int head;     // KV head
   int tok_off;  // token offset of the tile inside its block
   int nvalid;   // valid tokens of the tile (0: empty, loads return zeros)
+  int newrow;   // -1: a pool tile; else the tile is the step's token alone,
+                // read from row newrow (sequence x KV heads + head) of the
+                // step's K/V rows
 };
 
-template <int G, bool SPLIT>
+// Plan modes: kPlanHere plans on the device at start (one wave, from the
+// context lengths). kPlanCache also has a plan buffer: a workgroup whose
+// slot's header names this launch (mode, grid, batch, partition size and the
+// caller's plan epoch) loads its units and its waves' first block ids from
+// it instead; otherwise it plans and stores the slot for the launches after
+// it.
+constexpr int kPlanHere = 0, kPlanCache = 1;
+
+__device__ inline uint32_t plan_mode_word(bool split, int step) {
+  return (uint32_t)kPlanMagic | (split ? 1u : 0u) | (step ? 2u : 0u);
+}
+
+template <int G, bool SPLIT, int PM>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(DecodeParams p) {
   using C = CfgM<G>;
@@ -151,7 +172,7 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ int mg_bad[NW];
   __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
-  __shared__ int ubadpart[MAXU];   // part * 2 + bad
+  __shared__ int ubadpart[MAXU];   // part * 4 + 2 * append + bad
   __shared__ uint32_t act_lds[2];
 
   const int lane = threadIdx.x & 63;
@@ -162,16 +183,70 @@ void decode_mfma_kernel(DecodeParams p) {
   float *red = reinterpret_cast<float *>(vbuf);
 
   const int S = p.num_seqs, H = p.num_kv_heads, HQ = p.num_q_heads;
+  // A stored plan: the header (which launch it is for), this wave's first
+  // two block ids and (wave 0) the workgroup's unit slots, all loaded at once.
+  const __amdgpu_buffer_rsrc_t plan_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t *>(p.plan) + (int64_t)blockIdx.x * kPlanWgBytes, (short)0,
+      PM == kPlanHere ? 0 : kPlanWgBytes, 0x00020000);
+  bool use_plan = false;
+  int pre_id0 = 0, pre_id1 = 0;
+  const u32x4 want_hdr{plan_mode_word(SPLIT, p.step), gridDim.x, (uint32_t)S,
+                       (uint32_t)p.partition_size};
+  if constexpr (PM == kPlanCache) {
+    const u32x4 hdr = __builtin_amdgcn_raw_buffer_load_b128(plan_rsrc, kPlanHdr, 0, 0);
+    const uint32_t epoch = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanHdr + 16, 0, 0);
+    pre_id0 = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanIds + 8 * wave, 0, 0);
+    pre_id1 = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanIds + 8 * wave + 4, 0, 0);
+    use_plan = __builtin_amdgcn_readfirstlane(hdr[0]) == want_hdr[0] &&
+               __builtin_amdgcn_readfirstlane(hdr[1]) == want_hdr[1] &&
+               __builtin_amdgcn_readfirstlane(hdr[2]) == want_hdr[2] &&
+               __builtin_amdgcn_readfirstlane(hdr[3]) == want_hdr[3] &&
+               __builtin_amdgcn_readfirstlane(epoch) == p.plan_epoch;
+  }
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
-    plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
+    if (use_plan) {
+      // Slots are checked so that a plan made for other inputs can give
+      // wrong numbers but never an access outside the caller's buffers.
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(plan_rsrc, kPlanUnits + 16 * lane,
+                                                            0, 0);
+      const int bp = (int)__builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanBp + 4 * lane,
+                                                              0, 0);
+      my = make_int4((int)u[0], (int)u[1], (int)u[2], (int)u[3]);
+      const int cap = p.max_blocks_per_seq * p.block_size;
+      my_act = bp >= 0 && my.x >= 0 && my.x < S && my.y >= 0 && my.y < H && my.z >= 0 &&
+               my.z <= my.w && my.w <= cap && (bp >> 2) < (SPLIT ? p.max_parts : 1) &&
+               (p.step || (bp & 2) == 0);
+      my_bp = my_act ? bp : 0;
+      if (!my_act) my = make_int4(0, 0, 0, 0);
+    } else {
+      plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
+    }
     uinfo[lane] = my;
     ubadpart[lane] = my_bp;
     const uint64_t m = __builtin_amdgcn_ballot_w64(my_act != 0);
     if (lane == 0) {
       act_lds[0] = (uint32_t)m;
       act_lds[1] = (uint32_t)(m >> 32);
+    }
+    if constexpr (PM == kPlanCache) {
+      // Refresh the slot (the same values when it was used); stores that
+      // must not happen go past num_records and are dropped, so every path
+      // issues the same stores.
+      const int drop = use_plan ? kPlanWgBytes : 0;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{(uint32_t)my.x, (uint32_t)my.y, (uint32_t)my.z, (uint32_t)my.w}, plan_rsrc,
+          drop + kPlanUnits + 16 * lane, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(my_act ? (uint32_t)my_bp : 0xffffffffu, plan_rsrc,
+                                            drop + kPlanBp + 4 * lane, 0, 0);
+      const uint32_t hv = lane == 0   ? want_hdr[0]
+                          : lane == 1 ? want_hdr[1]
+                          : lane == 2 ? want_hdr[2]
+                          : lane == 3 ? want_hdr[3]
+                                      : p.plan_epoch;
+      __builtin_amdgcn_raw_buffer_store_b32(
+          hv, plan_rsrc, lane < 5 ? drop + kPlanHdr + 4 * lane : kPlanWgBytes, 0, 0);
     }
   }
   __syncthreads();
@@ -185,6 +260,8 @@ void decode_mfma_kernel(DecodeParams p) {
   const int64_t block_stride = head_stride * H;
   const uint8_t *kpool = reinterpret_cast<const uint8_t *>(p.key_cache);
   const uint8_t *vpool = reinterpret_cast<const uint8_t *>(p.value_cache);
+  const uint8_t *knew = reinterpret_cast<const uint8_t *>(p.new_key);
+  const uint8_t *vnew = reinterpret_cast<const uint8_t *>(p.new_value);
   const __amdgpu_buffer_rsrc_t tab_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(p.block_tables), (short)0,
       (int)((int64_t)S * p.max_blocks_per_seq * 4), 0x00020000);
@@ -210,9 +287,10 @@ void decode_mfma_kernel(DecodeParams p) {
     return c + (c & 1);
   };
 
-  // ---- Cursor over this wave's tile stream (uniform state).
+  // ---- Cursor over this wave's tile stream (uniform state). A unit is
+  // cur_np pool tiles, then (cur_app) one tile holding the step's token.
   uint64_t cur_mask = act_mask;
-  int cur_j = -1, cur_i = 0, cur_c = 0;
+  int cur_j = -1, cur_i = 0, cur_c = 0, cur_np = 0, cur_app = 0;
   int4 cur_u{0, 0, 0, 0};
   auto advance = [&]() {
     ++cur_i;
@@ -226,13 +304,18 @@ void decode_mfma_kernel(DecodeParams p) {
       cur_j = __builtin_ctzll(cur_mask);
       cur_mask &= cur_mask - 1;
       cur_u = info(cur_j);
-      cur_c = padded_count((cur_u.w - cur_u.z + TILE - 1) / TILE);
+      cur_app = (__builtin_amdgcn_readfirstlane(ubadpart[cur_j]) >> 1) & 1;
+      cur_np = (cur_u.w - cur_u.z + TILE - 1) / TILE;
+      cur_c = padded_count(cur_np + cur_app);
       cur_i = 0;
     }
   };
-  auto make_desc = [&]() -> DescM {
-    DescM d{0, 0, 0, 0};
-    const int tok0 = cur_u.z + (wave + cur_i * NW) * TILE;
+  // pre >= 0: the id was preloaded from the plan (stream position pre of
+  // this wave); the step's-token tile still looks its id up.
+  auto make_desc = [&](int pre = -1) -> DescM {
+    DescM d{0, 0, 0, 0, -1};
+    const int k = wave + cur_i * NW;
+    const int tok0 = cur_u.z + k * TILE;
     // The id load is issued on every path (an empty tile reads past the
     // table's num_records, which returns 0 without an access).
     int entry_off = 0x7ffffff0;
@@ -241,13 +324,24 @@ void decode_mfma_kernel(DecodeParams p) {
       d.head = cur_u.y;
       d.tok_off = tok0 % bs;
       d.nvalid = min(TILE, cur_u.w - tok0);
+    } else if (cur_j >= 0 && cur_app && k == cur_np) {
+      // The step's token (position cur_u.w = T - 1): its block id is still
+      // looked up, so a bad table entry poisons the unit as a pool read would.
+      entry_off = (cur_u.x * p.max_blocks_per_seq + cur_u.w / bs) * 4;
+      d.head = cur_u.y;
+      d.nvalid = 1;
+      d.newrow = cur_u.x * H + cur_u.y;
     }
-    d.blk = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, entry_off, 0, 0);
+    if (pre >= 0 && d.newrow < 0)
+      d.blk = pre == 0 ? pre_id0 : pre_id1;
+    else
+      d.blk = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, entry_off, 0, 0);
     return d;
   };
   // Buffer resource over the valid rows of one tile of a pool; an invalid
   // block id gives an empty resource (zeros, no access) and marks the tile.
-  auto tile_rsrc = [&](const DescM &d, const uint8_t *pool, int &nvalid, int &bad) {
+  auto tile_rsrc = [&](const DescM &d, const uint8_t *pool, const uint8_t *step_rows,
+                       int &nvalid, int &bad) {
     int blk = __builtin_amdgcn_readfirstlane(d.blk), n = d.nvalid;
     bad = 0;
     if (n > 0 && (blk < 0 || blk >= p.num_blocks)) {
@@ -256,8 +350,10 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     if (n <= 0) blk = 0;
     nvalid = n;
-    const uint8_t *base = pool + (int64_t)blk * block_stride + (int64_t)d.head * head_stride +
-                          (int64_t)d.tok_off * D * 2;
+    const uint8_t *base = d.newrow >= 0
+                              ? step_rows + (int64_t)d.newrow * (D * 2)
+                              : pool + (int64_t)blk * block_stride +
+                                    (int64_t)d.head * head_stride + (int64_t)d.tok_off * D * 2;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n * D * 2,
                                              0x00020000);
   };
@@ -265,7 +361,7 @@ void decode_mfma_kernel(DecodeParams p) {
   const int koff = (n16 & 7) * (2 * D) + 16 * grp + 64 * (n16 >> 3);
   auto load_k = [&](u32x4(&kt)[KL], const DescM &d) {
     int nv, bad;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(d, kpool, nv, bad);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(d, kpool, knew, nv, bad);
 #pragma unroll
     for (int i = 0; i < KL; ++i)
       kt[i] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -274,7 +370,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // V: load i gives lane l the 8 channels 8 (l % 32) .. of token 2i + l / 32.
   const int voff = lane * 16;
   auto load_v = [&](u32x4(&vt)[VL], const DescM &d, int &nvalid, int &bad) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(d, vpool, nvalid, bad);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(d, vpool, vnew, nvalid, bad);
 #pragma unroll
     for (int i = 0; i < VL; ++i)
       vt[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + i * 1024, 0, kStreamLoad);
@@ -288,9 +384,9 @@ void decode_mfma_kernel(DecodeParams p) {
   {
     cur_i = -1;
     advance();
-    const DescM d0 = make_desc();
+    const DescM d0 = make_desc(use_plan ? 0 : -1);
     advance();
-    const DescM d1 = make_desc();
+    const DescM d1 = make_desc(use_plan ? 1 : -1);
     load_k(ka, d0);
     load_v(va, d0, nv_a, bad_a);
     advance();
@@ -299,6 +395,15 @@ void decode_mfma_kernel(DecodeParams p) {
     load_v(vb, d1, nv_b, bad_b);
     advance();
     dn2 = make_desc();
+    if constexpr (PM == kPlanCache) {
+      // The wave's first two ids (every lane holds the same), stored for
+      // the launches after this one unless they came from the slot.
+      const int drop = use_plan || lane != 0 ? kPlanWgBytes : 0;
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)d0.blk, plan_rsrc,
+                                            drop + kPlanIds + 8 * wave, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)d1.blk, plan_rsrc,
+                                            drop + kPlanIds + 8 * wave + 4, 0, 0);
+    }
   }
 
   auto stage_queries = [&](uint64_t mask) {
@@ -417,8 +522,9 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     const int qslot = kq++;
     const int4 uj = info(j);
-    const int cpad = padded_count((uj.w - uj.z + TILE - 1) / TILE);
-    int ubad = __builtin_amdgcn_readfirstlane(ubadpart[j]) & 1;
+    const int ubp = __builtin_amdgcn_readfirstlane(ubadpart[j]);
+    const int cpad = padded_count((uj.w - uj.z + TILE - 1) / TILE + ((ubp >> 1) & 1));
+    int ubad = ubp & 1;
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = kNoMax;
@@ -478,7 +584,7 @@ void decode_mfma_kernel(DecodeParams p) {
     // exact for the loads in flight.
     static_assert(G * D / 4 <= NW * 64, "one channel quad per thread");
     const int64_t qrow = (int64_t)uj.x * HQ + (int64_t)uj.y * G;
-    const int part = __builtin_amdgcn_readfirstlane(ubadpart[j]) >> 1;
+    const int part = ubp >> 2;
     {
       const int idx = 4 * threadIdx.x;
       const bool live = idx < G * D;
@@ -536,40 +642,54 @@ void decode_mfma_kernel(DecodeParams p) {
 
 }  // namespace
 
-// Launch the matrix-core kernel when the shape is one it covers; false
-// otherwise (the caller then uses another kernel).
-bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
+int64_t decode_mfma_grid(const DecodeParams &p) {
   if (!p.kv_bf16 || p.kv_fp8 || p.head_dim != D || p.block_size % TILE != 0 || p.query_start_loc)
-    return false;
-  if (p.partition_size > 0 && p.partition_size % TILE != 0) return false;
-  if ((int64_t)p.num_seqs * p.max_blocks_per_seq * 4 > 0x7fffffff) return false;
+    return 0;
+  if (p.partition_size > 0 && p.partition_size % TILE != 0) return 0;
+  if ((int64_t)p.num_seqs * p.max_blocks_per_seq * 4 > 0x7fffffff) return 0;
   const int group = p.num_q_heads / p.num_kv_heads;
+  if (group < 1 || group > 8) return 0;
   const int64_t parts = p.partition_size > 0 ? p.max_parts : 1;
   const int64_t units = parts * p.num_seqs * p.num_kv_heads;
-  if (units <= 0 || units > 0x7fffffff) return false;
+  if (units <= 0 || units > 0x7fffffff) return 0;
   int64_t grid = num_cus();
   // Split mode takes the tiled kernel (a workgroup per unit) when the
   // persistent form cannot pay for its planner and ring: at most one unit
   // per CU, or partitions under 2 tiles per wavefront.
-  if (p.partition_size > 0 && (units <= grid || p.partition_size < 2 * NW * TILE)) return false;
+  if (p.partition_size > 0 && (units <= grid || p.partition_size < 2 * NW * TILE)) return 0;
   if (grid > units) grid = units;
-  if (grid * MAXU < units) return false;  // more than 64 units per workgroup
+  if (grid * MAXU < units) return 0;  // more than 64 units per workgroup
   const int64_t out_bytes = (int64_t)p.num_seqs * p.num_q_heads * parts * D *
                             (p.partition_size > 0 ? 4 : (p.out_bf16 ? 2 : 4));
-  if (out_bytes > 0x7fff0000) return false;
+  if (out_bytes > 0x7fff0000) return 0;
+  return grid;
+}
+
+template <int PM>
+static bool launch_mode(const DecodeParams &p, int64_t grid, hipStream_t stream) {
+  const int group = p.num_q_heads / p.num_kv_heads;
   const bool split = p.partition_size > 0;
   switch (group) {
-#define PA_CASE(g)                                                                  \
-  case g:                                                                           \
-    if (split)                                                                      \
-      decode_mfma_kernel<g, true><<<(unsigned)grid, NW * 64, 0, stream>>>(p);       \
-    else                                                                            \
-      decode_mfma_kernel<g, false><<<(unsigned)grid, NW * 64, 0, stream>>>(p);      \
+#define PA_CASE(g)                                                                   \
+  case g:                                                                            \
+    if (split)                                                                       \
+      decode_mfma_kernel<g, true, PM><<<(unsigned)grid, NW * 64, 0, stream>>>(p);    \
+    else                                                                             \
+      decode_mfma_kernel<g, false, PM><<<(unsigned)grid, NW * 64, 0, stream>>>(p);   \
     return true;
     PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
 #undef PA_CASE
     default: return false;
   }
+}
+
+// Launch the matrix-core kernel when the shape is one it covers; false
+// otherwise (the caller then uses another kernel).
+bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
+  const int64_t grid = decode_mfma_grid(p);
+  if (grid == 0) return false;
+  return p.plan ? launch_mode<kPlanCache>(p, grid, stream)
+                : launch_mode<kPlanHere>(p, grid, stream);
 }
 
 }  // namespace pa

@@ -61,7 +61,47 @@ struct DecodeParams {
   float v_scale;
   void *scratch;          // balanced kernels: merge entries + piece slots
   int64_t scratch_bytes;
+  // Decode step: non-null means position T_s - 1 of every sequence is this
+  // step's token and its K/V rows are read from here ([num_seqs][num_kv_heads]
+  // [head_dim], the pools' dtype) instead of from the pools. Only the
+  // matrix-core BF16 kernel accepts it; the others decline such a launch.
+  const void *new_key;
+  const void *new_value;
+  int32_t step;  // 1: a decode step (new_key/new_value set)
+  // Plan cache (matrix-core kernel only): a launch whose plan_epoch matches
+  // the slot it finds reads its units from there, else plans and stores them.
+  void *plan;
+  uint32_t plan_epoch;
 };
+
+// Plan buffer: per workgroup of the persistent decode grid kPlanWgBytes
+// bytes: the 64 unit slots (int4 sequence, KV head, first token, end of its
+// pool tokens), their int partition * 4 + 2 * step token + bad (-1: no
+// unit), each wave's first two block ids, and a header (mode word, grid,
+// batch size, partition size, epoch) naming the launch that wrote it.
+constexpr int kPlanWgBytes = 1536;
+constexpr int kPlanUnits = 0, kPlanBp = 1024, kPlanIds = 1280, kPlanHdr = 1344;
+constexpr int kPlanMagic = 0x504c0000;
+
+// The step's K/V rows written to position T_s - 1 of each sequence (the slot
+// its block table gives; a block id outside the pool, T_s = 0 or T_s past the
+// table's capacity writes nothing). Null new_key = no write.
+struct AppendArgs {
+  const void *new_key;
+  const void *new_value;
+  void *key_cache;
+  void *value_cache;
+  const int32_t *block_tables;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t row_bytes;  // head_dim x element bytes
+};
+
+// The append write on its own: one wavefront per (sequence, KV head).
+pa_status launch_append(const AppendArgs &a, const int32_t *context_lens, int32_t num_seqs,
+                        hipStream_t stream);
 
 // Balanced decode (every workgroup an equal share of the rounds). A unit
 // that crosses workgroup boundaries is computed in pieces; each piece's
@@ -100,6 +140,10 @@ bool launch_decode_tiled(const DecodeParams &p, unsigned grid, hipStream_t strea
 // Matrix-core decode for BF16, head_dim 256, block_size % 16 == 0 (decode
 // rows only). Returns false when the shape is not covered.
 bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
+// Persistent grid of the matrix-core kernel for p, or 0 when that kernel does
+// not take p (then neither a plan nor a planned launch applies).
+int64_t decode_mfma_grid(const DecodeParams &p);
+
 
 // Matrix-core decode over FP8 pools (head_dim 256, block_size % 16 == 0,
 // partitions of a multiple of 32 tokens). Returns false when the shape is
@@ -114,7 +158,8 @@ pa_status launch_read_probe(const void *pool, int64_t pool_bytes, const int32_t 
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
-                        int32_t max_parts, int32_t out_bf16, hipStream_t stream);
+                        int32_t max_parts, int32_t out_bf16, hipStream_t stream,
+                        const AppendArgs *append = nullptr);
 
 struct PrefillParams {
   void *out;

@@ -3,6 +3,7 @@
 
 #include "launch.h"
 #include "pa_internal.h"
+#include "persistent_plan.h"
 
 namespace {
 
@@ -568,6 +569,147 @@ extern "C" pa_status pa_reduce(void *out, const float *part_out, const float *pa
     return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
   return pa::launch_reduce(out, part_out, part_max, part_sum, context_lens, num_seqs, num_q_heads,
                            head_dim, partition_size, max_parts, out_dtype == PA_BF16, stream);
+}
+
+extern "C" pa_status pa_decode_step(void *out, float *part_out, float *part_max,
+                                    float *part_sum, const void *query, const void *key,
+                                    const void *value, void *key_cache, void *value_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                                    int32_t partition_size, int32_t max_parts, pa_dtype kv_dtype,
+                                    pa_dtype out_dtype, void *plan, uint32_t plan_epoch,
+                                    hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_step";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (!dtype_ok(out_dtype)) return pa::fail(PA_EINVAL, "%s: bad out_dtype", fn);
+  const bool split = partition_size != 0;
+  if (split) {
+    if (partition_size < 16 || partition_size % block_size != 0)
+      return pa::fail(PA_EINVAL,
+                      "%s: partition_size=%d must be 0 or >= 16 and a multiple of block_size=%d",
+                      fn, partition_size, block_size);
+    if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key || !value || !key_cache || !value_cache || !block_tables ||
+      !context_lens || (split && (!part_out || !part_max || !part_sum)))
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+
+  pa::AppendArgs a{};
+  a.new_key = key;
+  a.new_value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.row_bytes = head_dim * (kv_dtype == PA_BF16 ? 2 : 4);
+
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = split ? partition_size : 0;
+  p.max_parts = split ? max_parts : 1;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.out_bf16 = out_dtype == PA_BF16;
+
+  // The matrix-core kernel reads the step's token from key/value, so the
+  // slot write can follow it (inside the merge launch when there is one).
+  // Other kernels read it from the pool: the write goes first.
+  p.new_key = key;
+  p.new_value = value;
+  p.step = 1;
+  p.plan = plan;
+  p.plan_epoch = plan_epoch;
+  const bool fused = pa::launch_decode_mfma(p, stream);
+  if (fused) {
+    st = pa::check_launch(fn);
+  } else {
+    p.new_key = p.new_value = nullptr;
+    p.step = 0;
+    p.plan = nullptr;
+    st = pa::launch_append(a, context_lens, num_seqs, stream);
+    if (st == PA_OK) st = pa::launch_decode(p, stream);
+  }
+  if (st != PA_OK) return st;
+  if (split)
+    return pa::launch_reduce(out, part_out, part_max, part_sum, context_lens, num_seqs,
+                             num_q_heads, head_dim, partition_size, max_parts,
+                             out_dtype == PA_BF16, stream, fused ? &a : nullptr);
+  return fused ? pa::launch_append(a, context_lens, num_seqs, stream) : PA_OK;
+}
+
+extern "C" size_t pa_decode_plan_bytes(void) {
+  return (size_t)pa::persist::num_cus() * pa::kPlanWgBytes;
+}
+
+extern "C" pa_status pa_decode_partitioned_planned(
+    float *part_out, float *part_max, float *part_sum, const void *query, const void *key_cache,
+    const void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+    int32_t partition_size, int32_t max_parts, pa_dtype kv_dtype, void *plan,
+    uint32_t plan_epoch, hipStream_t stream) {
+  pa::clear_error();
+  const char *fn = "pa_decode_partitioned_planned";
+  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, scale,
+                                       kv_dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size % block_size != 0)
+    return pa::fail(PA_EINVAL, "%s: partition_size=%d must be >= 16 and a multiple of block_size=%d",
+                    fn, partition_size, block_size);
+  if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
+  if (num_seqs == 0) return PA_OK;
+  if (!part_out || !part_max || !part_sum || !query || !key_cache || !value_cache ||
+      !block_tables || !context_lens)
+    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
+  pa::DecodeParams p{};
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.part_out = part_out;
+  p.part_max = part_max;
+  p.part_sum = part_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.partition_size = partition_size;
+  p.max_parts = max_parts;
+  p.kv_bf16 = kv_dtype == PA_BF16;
+  p.plan = plan;
+  p.plan_epoch = plan_epoch;
+  return pa::launch_decode(p, stream);
 }
 
 extern "C" pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,

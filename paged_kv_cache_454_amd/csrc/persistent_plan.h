@@ -82,7 +82,8 @@ __device__ __forceinline__ int upper_index(const int *incl, int off) {
 }
 
 // The workgroup's units, one per lane: lane k holds the unit assigned in
-// round k. Units are enumerated as all full partitions (sequence-major)
+// round k, as (sequence, KV head, first token, end of its pool tokens) and
+// partition * 4 + 2 * (takes the step's token from new_key/new_value) + bad. Units are enumerated as all full partitions (sequence-major)
 // followed by the last, partial partitions ordered by decreasing size (for
 // up to 64 sequences; in sequence order beyond that), and dealt to the
 // workgroups in snake order (round k goes 0..grid-1 when k is even,
@@ -197,8 +198,11 @@ __device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int
     lo = c_p * P;
     hi = c_T < lo + P ? c_T : lo + P;
   }
-  unit = make_int4(c_s, c_h, lo, hi);
-  bad_part = c_p * 2 + c_bad;
+  // A decode step's last unit of a sequence takes its final token from the
+  // step's K/V rows: the pool part of the unit ends one token earlier.
+  const int app = p.step && c_T > 0 && hi == c_T && !c_bad;
+  unit = make_int4(c_s, c_h, lo, hi - app);
+  bad_part = c_p * 4 + app * 2 + c_bad;
 }
 
 // Compute units of the current device (cached per device).

@@ -14,8 +14,14 @@
 // ends at the last valid partition, so loads past it return zeros without a
 // memory access and need no branch. Each lane owns VEC channels of a row (a
 // lane past head_dim reads the next partition's channels and discards them).
+//
+// In a decode step the same launch also writes the step's K/V rows to their
+// slots (the decode kernel before it read them from the step's rows, not
+// from the pool): the wavefront of each KV head's first query head issues
+// those loads beside its round trip 2 and stores them at the end.
 #include <math.h>
 
+#include "append_rows.h"
 #include "launch.h"
 #include "pa_device.h"
 
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(void *out, const float *__r
                                                      const int32_t *__restrict__ context_lens,
                                                      int rows, int num_q_heads, int head_dim,
                                                      int partition_size, int max_parts,
-                                                     int out_bf16) {
+                                                     int out_bf16, AppendArgs app) {
   const int lane = threadIdx.x & 63;
   // sequence * num_q_heads + head, uniform per wavefront
   const int sh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -80,6 +86,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(void *out, const float *__r
   const int64_t n64 = ((int64_t)T + partition_size - 1) / partition_size;
   const bool bad = n64 > max_parts;
   const int n = bad ? 0 : (int)n64;
+
+  const int group = app.new_key ? num_q_heads / app.num_kv_heads : 1;
+  const int qh = sh - seq * num_q_heads;
+  const bool writer = app.new_key != nullptr && qh % group == 0;  // uniform
+  AppendLoad al{};
+  if (writer) al = append_issue(app, seq, qh / group, T, lane);
 
   // M over the valid partitions (fmaxf skips a NaN record; its NaN weight
   // still poisons the row below).
@@ -133,6 +145,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(void *out, const float *__r
                   out_bf16);
     }
   }
+  if (writer) append_commit(app, al, qh / group, lane);
 }
 
 }  // namespace
@@ -140,7 +153,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(void *out, const float *__r
 pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
                         const float *part_sum, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
-                        int32_t max_parts, int32_t out_bf16, hipStream_t stream) {
+                        int32_t max_parts, int32_t out_bf16, hipStream_t stream,
+                        const AppendArgs *append) {
+  AppendArgs app{};
+  if (append) {
+    app = *append;
+    if (app.row_bytes % 16 != 0 || app.row_bytes / 16 * 2 > 64 * kAppendPieces ||
+        app.num_kv_heads <= 0 || num_q_heads % app.num_kv_heads != 0)
+      return fail(PA_EUNSUPPORTED, "decode step: %d-byte rows", app.row_bytes);
+  }
   if (max_parts > kReduceMaxParts)
     return fail(PA_EUNSUPPORTED, "pa_reduce: max_parts=%d > %d", max_parts, kReduceMaxParts);
   const int64_t rows = (int64_t)num_seqs * num_q_heads;
@@ -152,11 +173,11 @@ pa_status launch_reduce(void *out, const float *part_out, const float *part_max,
   if (head_dim % 4 == 0)
     reduce_kernel<4><<<grid, 256, 0, stream>>>(out, part_out, part_max, part_sum, context_lens,
                                                (int)rows, num_q_heads, head_dim, partition_size,
-                                               max_parts, out_bf16);
+                                               max_parts, out_bf16, app);
   else
     reduce_kernel<1><<<grid, 256, 0, stream>>>(out, part_out, part_max, part_sum, context_lens,
                                                (int)rows, num_q_heads, head_dim, partition_size,
-                                               max_parts, out_bf16);
+                                               max_parts, out_bf16, app);
   return check_launch("pa_reduce");
 }
 

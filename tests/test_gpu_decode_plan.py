@@ -1,0 +1,161 @@
+"""Decode plan buffers: the first launch of an epoch plans and stores its
+deal of units, later launches of the same epoch read it. Either way a launch
+deals the same units to the same workgroups as one without a buffer, so its
+outputs must be bit for bit the unplanned call's; slots tagged for another
+launch (mode, partition size) or holding zeros must be detected and replanned
+(again the same bits). The step's outputs are also compared with the oracle
+directly."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_454_amd as pa
+from oracle import attention as oracle
+from paged_kv_cache_454_amd import inputs
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _parts(case, P):
+    S, H, D = case.query.shape
+    mp = G.max_parts_for(case, P)
+    return (torch.full((S, H, mp, D), float("nan"), device=G.DEV),
+            torch.full((S, H, mp), float("nan"), device=G.DEV),
+            torch.full((S, H, mp), float("nan"), device=G.DEV))
+
+
+def _partitioned(t, case, P, plan=None, epoch=0):
+    po, pm, ps = _parts(case, P)
+    args = (po, pm, ps, t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+            t["context_lens"], case.scale, P)
+    if plan is None:
+        pa.pa_decode_partitioned(*args)
+    else:
+        pa.pa_decode_partitioned_planned(*args, plan, epoch)
+    return [G.bits(x) for x in (po, pm, ps)]
+
+
+def _step(case, P, plan=None, epoch=0, t=None):
+    t = G.to_dev(case) if t is None else t
+    S, H, D = case.query.shape
+    out = torch.full((S, H, D), float("nan"), device=G.DEV)
+    po, pm, ps = _parts(case, P) if P else (None, None, None)
+    pa.pa_decode_step(out, t["query"], t["key"], t["value"], t["key_cache"], t["value_cache"],
+                      t["block_tables"], t["context_lens"], case.scale, P, po, pm, ps,
+                      plan=plan, plan_epoch=epoch)
+    return out, t
+
+
+def _oracle_step(case):
+    kc, vc = oracle.cache_write(case.key_cache, case.value_cache, case.key, case.value,
+                                case.slot_mapping, case.block_size)
+    return oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens,
+                         case.block_size, case.scale)
+
+
+@pytest.mark.parametrize("preset", ["mixed", "long"])
+def test_planned_partitioned_bitexact(preset):
+    """First launch with a fresh epoch plans and writes the buffer, the next
+    ones read it; all give the unplanned bits."""
+    print(f"[plan] partitioned preset={preset}", flush=True)
+    case = inputs.preset_case(preset, seed=0)
+    t = G.to_dev(case)
+    G.write(t)
+    P = G.bench_partitions()[0][preset]
+    plan = pa.decode_plan_buffer()
+    want = _partitioned(t, case, P)
+    for _ in range(3):
+        for a, b in zip(want, _partitioned(t, case, P, plan, 11)):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("preset", ["mixed", "long"])
+def test_planned_step_bitexact_and_oracle(preset):
+    print(f"[plan] step preset={preset}", flush=True)
+    case = inputs.preset_case(preset, seed=0)
+    P = G.bench_partitions()[0][preset]
+    base, tb = _step(case, P)
+    plan = pa.decode_plan_buffer()
+    want = _oracle_step(case)
+    for _ in range(2):           # writes the plan, then reads it
+        got, t = _step(case, P, plan, 5)
+        assert np.array_equal(G.bits(base), G.bits(got))
+        assert np.array_equal(G.bits(tb["key_cache"]), G.bits(t["key_cache"]))
+        assert np.array_equal(G.bits(tb["value_cache"]), G.bits(t["value_cache"]))
+        assert G.max_err(G.host(got), want) <= G.BF16_TOL
+
+
+EDGE_LENS = ([1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1025, 2049, 4097]
+             + [int(x) for x in np.random.default_rng(3).integers(1, 3000, 83)])
+
+
+@pytest.mark.parametrize("P", [0, 256, 1024])
+def test_planned_step_edges(P):
+    print(f"[plan] step edges P={P}", flush=True)
+    case = inputs.decode_case(EDGE_LENS, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2,
+                              seed=P + 1, kv_bias_scale=3.0)
+    base, _ = _step(case, P)
+    plan = pa.decode_plan_buffer()
+    want = _oracle_step(case)
+    for _ in range(2):
+        got, _ = _step(case, P, plan, 3)
+        assert np.array_equal(G.bits(base), G.bits(got))
+        assert G.max_err(G.host(got), want) <= G.BF16_TOL
+
+
+def test_epochs_across_steps():
+    """Three steps of one growing batch (every sequence one token longer each
+    step, new tables and pools each time) through one plan buffer, a new
+    epoch per step: every step matches the oracle and its unplanned bits."""
+    plan = pa.decode_plan_buffer()
+    lens = np.array(EDGE_LENS)
+    for k in range(3):
+        case = inputs.decode_case(lens + k, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2,
+                                  seed=40 + k)
+        base, _ = _step(case, 512)
+        for _ in range(2):
+            got, _ = _step(case, 512, plan, 100 + k)
+            assert np.array_equal(G.bits(base), G.bits(got)), k
+        assert G.max_err(G.host(got), _oracle_step(case)) <= G.BF16_TOL
+
+
+def test_mismatched_plans_are_replanned():
+    """Slots written by a step launch, by a launch at another partition
+    size, or zeros, under the same epoch: the tags differ, so each launch
+    plans for itself (and rewrites the slots)."""
+    case = inputs.decode_case(EDGE_LENS, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2, seed=8)
+    P = 512
+    t = G.to_dev(case)
+    G.write(t)
+    want = _partitioned(t, case, P)
+    plan = pa.decode_plan_buffer()
+    _step(case, P, plan, 9)                          # slots tagged for the step
+    for a, b in zip(want, _partitioned(t, case, P, plan, 9)):
+        assert np.array_equal(a, b)
+    _partitioned(t, case, 1024, plan, 9)             # tagged for P = 1024
+    for a, b in zip(want, _partitioned(t, case, P, plan, 9)):
+        assert np.array_equal(a, b)
+    plan.zero_()
+    for a, b in zip(want, _partitioned(t, case, P, plan, 0)):
+        assert np.array_equal(a, b)
+    base, _ = _step(case, P)
+    got, _ = _step(case, P, plan, 9)                 # slots tagged for partitioned
+    assert np.array_equal(G.bits(base), G.bits(got))
+
+
+def test_plan_not_applicable_shapes():
+    """Where the matrix-core kernel does not take the batch (one unit per
+    compute unit; another head size) the buffer is left alone and the planned
+    calls give the unplanned results."""
+    for lens, d, P in (([2048] * 8, 256, 256), ([300, 40], 128, 256)):
+        case = inputs.decode_case(lens, 24, 4, d, 16, dtype="bf16", seed=2)
+        t = G.to_dev(case)
+        G.write(t)
+        buf = torch.zeros(pa.pa_decode_plan_bytes(), dtype=torch.uint8, device=G.DEV)
+        want = _partitioned(t, case, P)
+        for a, b in zip(want, _partitioned(t, case, P, buf, 1)):
+            assert np.array_equal(a, b)
+        torch.cuda.synchronize()
+        assert int(buf.sum()) == 0
