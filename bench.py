@@ -517,7 +517,8 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     """The same decode step over FP8 (E4M3FN) pools: each layer's BF16 pools
     are converted to codes of value / scale before timing (input
     preparation); one step = per layer the quantising write of the step's new
-    K/V (pa_reshape_and_cache_fp8), pa_decode_partitioned_fp8 and pa_reduce."""
+    K/V (pa_reshape_and_cache_fp8), pa_decode_partitioned_fp8 (planned: the
+    step's first layer plans, the others read its plan) and pa_reduce."""
     import numpy as np
     import torch
 
@@ -547,10 +548,15 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     scale = meta["scale"]
     stream = torch.cuda.current_stream()
 
+    plan = pa.decode_plan_buffer(dev)
+    epoch = [0]
+
     def decode(li):
         kc, vc = pools[li]
+        if li == 0:
+            epoch[0] += 1
         pa.pa_decode_partitioned_fp8(po, pm, ps, layers[li]["query"], kc, vc, bt, cl, scale, ks,
-                                     vs, P, stream=stream)
+                                     vs, P, stream=stream, plan=plan, plan_epoch=epoch[0])
 
     def step():
         for li, L in enumerate(layers):
@@ -576,12 +582,12 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     torch.cuda.empty_cache()
     return {
         "what": f"the decode step over FP8 E4M3FN pools (scales k {ks}, v {vs}): per pool set "
-                "pa_reshape_and_cache_fp8 + pa_decode_partitioned_fp8 + pa_reduce",
+                "pa_reshape_and_cache_fp8 + pa_decode_partitioned_fp8_planned + pa_reduce",
         "ms_per_step": round(ms_step, 5),
         "tokens_per_s": round(S * sets / (ms_step * 1e-3), 1),
         "kv_gbs_effective": round(kv_bytes_layer * len(layers) / (ms_step * 1e-3) / 1e9, 2),
         "partition_size": P,
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned_fp8",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partitioned_fp8_planned",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": decode_traffic("fp8", workload, P, seed),

@@ -501,6 +501,21 @@ pa_status pa_decode_partitioned_fp8(float *part_out, float *part_max, float *par
                                     float v_scale, int32_t partition_size, int32_t max_parts,
                                     hipStream_t stream);
 
+/* pa_decode_partitioned_fp8 with a plan buffer and epoch (see
+ * pa_decode_plan_bytes); a BF16 launch's slots are not read here, nor the
+ * other way round. Results bit for bit pa_decode_partitioned_fp8's. */
+pa_status pa_decode_partitioned_fp8_planned(float *part_out, float *part_max, float *part_sum,
+                                            const void *query, const uint8_t *key_cache,
+                                            const uint8_t *value_cache,
+                                            const int32_t *block_tables,
+                                            const int32_t *context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size,
+                                            int32_t max_blocks_per_seq, int32_t num_blocks,
+                                            float scale, float k_scale, float v_scale,
+                                            int32_t partition_size, int32_t max_parts,
+                                            void *plan, uint32_t plan_epoch, hipStream_t stream);
+
 /*
  * Host block allocator ([P2] s.2 "On-Demand Allocation": blocks are handed
  * out only as tokens arrive, so only a sequence's last block has unused

@@ -34,6 +34,9 @@ SIGNATURES = {
                             _f32, _f32, _f32, _st, _p]),
     "pa_decode_partitioned_fp8": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _f32, _f32, _f32, _i32, _i32, _p]),
+    "pa_decode_partitioned_fp8_planned": (_st, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+                                                _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
+                                                _i32, _i32, _p, _u32, _p]),
     "pa_decode": (_st, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _st, _st, _p]),
     "pa_partition_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),

@@ -331,8 +331,9 @@ def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens
 
 def pa_decode_partitioned_fp8(part_out, part_max, part_sum, query, key_cache, value_cache,
                               block_tables, context_lens, scale, k_scale, v_scale,
-                              partition_size, stream=None):
-    """pa_decode_partitioned over FP8 pools; pa_reduce merges the partitions."""
+                              partition_size, stream=None, plan=None, plan_epoch=0):
+    """pa_decode_partitioned over FP8 pools; pa_reduce merges the partitions.
+    With plan (a decode_plan_buffer()) and plan_epoch: the planned call."""
     num_blocks, hkv, bs, d, num_seqs = _attn_common(query, key_cache, value_cache, block_tables,
                                                     context_lens, "num_seqs", fp8=True)
     hq = query.shape[1]
@@ -344,13 +345,18 @@ def pa_decode_partitioned_fp8(part_out, part_max, part_sum, query, key_cache, va
     for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
         if tuple(t.shape) != (num_seqs, hq, max_parts):
             raise ValueError(f"{nm} must be float32 [num_seqs][num_q_heads][max_parts]")
-    check(lib().pa_decode_partitioned_fp8(
-        _dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
-        _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
-        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), block_tables.data_ptr(),
-        context_lens.data_ptr(), num_seqs, hq, hkv, d, bs, block_tables.shape[1], num_blocks,
-        float(scale), float(k_scale), float(v_scale), int(partition_size), max_parts,
-        _stream(stream)))
+    args = [_dev(part_out, "part_out", torch.float32), _dev(part_max, "part_max", torch.float32),
+            _dev(part_sum, "part_sum", torch.float32), _dev(query, "query"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            block_tables.data_ptr(), context_lens.data_ptr(), num_seqs, hq, hkv, d, bs,
+            block_tables.shape[1], num_blocks, float(scale), float(k_scale), float(v_scale),
+            int(partition_size), max_parts]
+    if plan is None:
+        check(lib().pa_decode_partitioned_fp8(*args, _stream(stream)))
+    else:
+        check(lib().pa_decode_partitioned_fp8_planned(*args, _plan(plan),
+                                                      int(plan_epoch) & 0xffffffff,
+                                                      _stream(stream)))
 
 
 def pa_reduce(out, part_out, part_max, part_sum, context_lens, partition_size, stream=None):

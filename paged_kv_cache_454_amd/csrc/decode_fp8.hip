@@ -155,6 +155,10 @@ struct Desc8 {
   int nvalid;      // valid tokens of the tile (0: empty, loads return zeros)
 };
 
+// Plan-cache kind of this kernel's slots (the two halves' block ids of each
+// wave's first two tiles).
+constexpr uint32_t kPlanKindFp8 = 0x200;
+
 template <int G, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_fp8_kernel(DecodeParams p) {
@@ -164,7 +168,7 @@ void decode_fp8_kernel(DecodeParams p) {
   __shared__ int mg_bad[NW];
   __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
-  __shared__ int ubadpart[MAXU];   // part * 4 + 2 * append + bad (append unused here)
+  __shared__ int ubadpart[MAXU];   // part * 4 + bad (no step tokens here)
   __shared__ uint32_t act_lds[2];
 
   const int lane = threadIdx.x & 63;
@@ -174,10 +178,17 @@ void decode_fp8_kernel(DecodeParams p) {
   float *red = red_all[wave];
 
   const int S = p.num_seqs, H = p.num_kv_heads, HQ = p.num_q_heads;
+  // With a plan buffer: the slot, this wave's first four block ids and (wave
+  // 0) the units, loaded together when the slot's tag names this launch.
+  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindFp8);
+  int pre_id[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pre_id[k] = plan_load_id(ps, wave, k);
+  const bool use_plan = ps.use;
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
-    plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
+    plan_or_load_units<SPLIT>(p, ps, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
     uinfo[lane] = my;
     ubadpart[lane] = my_bp;
     const uint64_t m = __builtin_amdgcn_ballot_w64(my_act != 0);
@@ -239,7 +250,8 @@ void decode_fp8_kernel(DecodeParams p) {
       cur_i = 0;
     }
   };
-  auto make_desc = [&]() -> Desc8 {
+  // pre >= 0: the ids were preloaded from the plan (stream position pre).
+  auto make_desc = [&](int pre = -1) -> Desc8 {
     Desc8 d{0, 0, 0, 0, 0, 0};
     const int tok0 = cur_u.z + (wave + cur_i * NW) * TILE;
     // Both id loads are issued on every path (an absent half reads past the
@@ -256,8 +268,13 @@ void decode_fp8_kernel(DecodeParams p) {
         d.off1 = (tok0 + HALF) % bs;
       }
     }
-    d.blk0 = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, e0, 0, 0);
-    d.blk1 = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, e1, 0, 0);
+    if (pre >= 0) {
+      d.blk0 = pre ? pre_id[2] : pre_id[0];
+      d.blk1 = pre ? pre_id[3] : pre_id[1];
+    } else {
+      d.blk0 = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, e0, 0, 0);
+      d.blk1 = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, e1, 0, 0);
+    }
     return d;
   };
   // Valid tokens and block ids of the two halves; an invalid id empties its
@@ -330,9 +347,9 @@ void decode_fp8_kernel(DecodeParams p) {
   {
     cur_i = -1;
     advance();
-    const Desc8 d0 = make_desc();
+    const Desc8 d0 = make_desc(use_plan ? 0 : -1);
     advance();
-    const Desc8 d1 = make_desc();
+    const Desc8 d1 = make_desc(use_plan ? 1 : -1);
     load_k(ka, d0);
     load_v(va, d0, nv_a, bad_a);
     advance();
@@ -341,6 +358,10 @@ void decode_fp8_kernel(DecodeParams p) {
     load_v(vb, d1, nv_b, bad_b);
     advance();
     dn2 = make_desc();
+    plan_store_id(ps, wave, 0, lane, d0.blk0);
+    plan_store_id(ps, wave, 1, lane, d0.blk1);
+    plan_store_id(ps, wave, 2, lane, d1.blk0);
+    plan_store_id(ps, wave, 3, lane, d1.blk1);
   }
 
   auto stage_queries = [&](uint64_t mask) {

@@ -149,19 +149,10 @@ struct DescM {
                 // step's K/V rows
 };
 
-// Plan modes: kPlanHere plans on the device at start (one wave, from the
-// context lengths). kPlanCache also has a plan buffer: a workgroup whose
-// slot's header names this launch (mode, grid, batch, partition size and the
-// caller's plan epoch) loads its units and its waves' first block ids from
-// it instead; otherwise it plans and stores the slot for the launches after
-// it.
-constexpr int kPlanHere = 0, kPlanCache = 1;
+// Plan-cache kind of this kernel's slots (first two block ids per wave).
+constexpr uint32_t kPlanKindMfma = 0x100;
 
-__device__ inline uint32_t plan_mode_word(bool split, int step) {
-  return (uint32_t)kPlanMagic | (split ? 1u : 0u) | (step ? 2u : 0u);
-}
-
-template <int G, bool SPLIT, int PM>
+template <int G, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(DecodeParams p) {
   using C = CfgM<G>;
@@ -183,70 +174,22 @@ void decode_mfma_kernel(DecodeParams p) {
   float *red = reinterpret_cast<float *>(vbuf);
 
   const int S = p.num_seqs, H = p.num_kv_heads, HQ = p.num_q_heads;
-  // A stored plan: the header (which launch it is for), this wave's first
-  // two block ids and (wave 0) the workgroup's unit slots, all loaded at once.
-  const __amdgpu_buffer_rsrc_t plan_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<uint8_t *>(p.plan) + (int64_t)blockIdx.x * kPlanWgBytes, (short)0,
-      PM == kPlanHere ? 0 : kPlanWgBytes, 0x00020000);
-  bool use_plan = false;
-  int pre_id0 = 0, pre_id1 = 0;
-  const u32x4 want_hdr{plan_mode_word(SPLIT, p.step), gridDim.x, (uint32_t)S,
-                       (uint32_t)p.partition_size};
-  if constexpr (PM == kPlanCache) {
-    const u32x4 hdr = __builtin_amdgcn_raw_buffer_load_b128(plan_rsrc, kPlanHdr, 0, 0);
-    const uint32_t epoch = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanHdr + 16, 0, 0);
-    pre_id0 = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanIds + 8 * wave, 0, 0);
-    pre_id1 = __builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanIds + 8 * wave + 4, 0, 0);
-    use_plan = __builtin_amdgcn_readfirstlane(hdr[0]) == want_hdr[0] &&
-               __builtin_amdgcn_readfirstlane(hdr[1]) == want_hdr[1] &&
-               __builtin_amdgcn_readfirstlane(hdr[2]) == want_hdr[2] &&
-               __builtin_amdgcn_readfirstlane(hdr[3]) == want_hdr[3] &&
-               __builtin_amdgcn_readfirstlane(epoch) == p.plan_epoch;
-  }
+  // With a plan buffer: this workgroup's slot, this wave's first two block
+  // ids and (wave 0) the units, loaded together when the slot's tag names
+  // this launch; otherwise planned here and stored.
+  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindMfma);
+  const int pre_id0 = plan_load_id(ps, wave, 0), pre_id1 = plan_load_id(ps, wave, 1);
+  const bool use_plan = ps.use;
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
-    if (use_plan) {
-      // Slots are checked so that a plan made for other inputs can give
-      // wrong numbers but never an access outside the caller's buffers.
-      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(plan_rsrc, kPlanUnits + 16 * lane,
-                                                            0, 0);
-      const int bp = (int)__builtin_amdgcn_raw_buffer_load_b32(plan_rsrc, kPlanBp + 4 * lane,
-                                                              0, 0);
-      my = make_int4((int)u[0], (int)u[1], (int)u[2], (int)u[3]);
-      const int cap = p.max_blocks_per_seq * p.block_size;
-      my_act = bp >= 0 && my.x >= 0 && my.x < S && my.y >= 0 && my.y < H && my.z >= 0 &&
-               my.z <= my.w && my.w <= cap && (bp >> 2) < (SPLIT ? p.max_parts : 1) &&
-               (p.step || (bp & 2) == 0);
-      my_bp = my_act ? bp : 0;
-      if (!my_act) my = make_int4(0, 0, 0, 0);
-    } else {
-      plan_units<SPLIT>(p, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
-    }
+    plan_or_load_units<SPLIT>(p, ps, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
     uinfo[lane] = my;
     ubadpart[lane] = my_bp;
     const uint64_t m = __builtin_amdgcn_ballot_w64(my_act != 0);
     if (lane == 0) {
       act_lds[0] = (uint32_t)m;
       act_lds[1] = (uint32_t)(m >> 32);
-    }
-    if constexpr (PM == kPlanCache) {
-      // Refresh the slot (the same values when it was used); stores that
-      // must not happen go past num_records and are dropped, so every path
-      // issues the same stores.
-      const int drop = use_plan ? kPlanWgBytes : 0;
-      __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{(uint32_t)my.x, (uint32_t)my.y, (uint32_t)my.z, (uint32_t)my.w}, plan_rsrc,
-          drop + kPlanUnits + 16 * lane, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(my_act ? (uint32_t)my_bp : 0xffffffffu, plan_rsrc,
-                                            drop + kPlanBp + 4 * lane, 0, 0);
-      const uint32_t hv = lane == 0   ? want_hdr[0]
-                          : lane == 1 ? want_hdr[1]
-                          : lane == 2 ? want_hdr[2]
-                          : lane == 3 ? want_hdr[3]
-                                      : p.plan_epoch;
-      __builtin_amdgcn_raw_buffer_store_b32(
-          hv, plan_rsrc, lane < 5 ? drop + kPlanHdr + 4 * lane : kPlanWgBytes, 0, 0);
     }
   }
   __syncthreads();
@@ -395,15 +338,10 @@ void decode_mfma_kernel(DecodeParams p) {
     load_v(vb, d1, nv_b, bad_b);
     advance();
     dn2 = make_desc();
-    if constexpr (PM == kPlanCache) {
-      // The wave's first two ids (every lane holds the same), stored for
-      // the launches after this one unless they came from the slot.
-      const int drop = use_plan || lane != 0 ? kPlanWgBytes : 0;
-      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)d0.blk, plan_rsrc,
-                                            drop + kPlanIds + 8 * wave, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)d1.blk, plan_rsrc,
-                                            drop + kPlanIds + 8 * wave + 4, 0, 0);
-    }
+    // The wave's first two ids, stored for the launches after this one
+    // unless they came from the slot (dropped stores otherwise).
+    plan_store_id(ps, wave, 0, lane, d0.blk);
+    plan_store_id(ps, wave, 1, lane, d1.blk);
   }
 
   auto stage_queries = [&](uint64_t mask) {
@@ -665,31 +603,25 @@ int64_t decode_mfma_grid(const DecodeParams &p) {
   return grid;
 }
 
-template <int PM>
-static bool launch_mode(const DecodeParams &p, int64_t grid, hipStream_t stream) {
-  const int group = p.num_q_heads / p.num_kv_heads;
-  const bool split = p.partition_size > 0;
-  switch (group) {
-#define PA_CASE(g)                                                                   \
-  case g:                                                                            \
-    if (split)                                                                       \
-      decode_mfma_kernel<g, true, PM><<<(unsigned)grid, NW * 64, 0, stream>>>(p);    \
-    else                                                                             \
-      decode_mfma_kernel<g, false, PM><<<(unsigned)grid, NW * 64, 0, stream>>>(p);   \
-    return true;
-    PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
-#undef PA_CASE
-    default: return false;
-  }
-}
-
 // Launch the matrix-core kernel when the shape is one it covers; false
 // otherwise (the caller then uses another kernel).
 bool launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = decode_mfma_grid(p);
   if (grid == 0) return false;
-  return p.plan ? launch_mode<kPlanCache>(p, grid, stream)
-                : launch_mode<kPlanHere>(p, grid, stream);
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const bool split = p.partition_size > 0;
+  switch (group) {
+#define PA_CASE(g)                                                                \
+  case g:                                                                         \
+    if (split)                                                                    \
+      decode_mfma_kernel<g, true><<<(unsigned)grid, NW * 64, 0, stream>>>(p);     \
+    else                                                                          \
+      decode_mfma_kernel<g, false><<<(unsigned)grid, NW * 64, 0, stream>>>(p);    \
+    return true;
+    PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
+#undef PA_CASE
+    default: return false;
+  }
 }
 
 }  // namespace pa

@@ -80,7 +80,8 @@ struct DecodeParams {
 // unit), each wave's first two block ids, and a header (mode word, grid,
 // batch size, partition size, epoch) naming the launch that wrote it.
 constexpr int kPlanWgBytes = 1536;
-constexpr int kPlanUnits = 0, kPlanBp = 1024, kPlanIds = 1280, kPlanHdr = 1344;
+constexpr int kPlanUnits = 0, kPlanBp = 1024, kPlanIds = 1280, kPlanHdr = 1408;
+constexpr int kPlanIdBytes = 16;  // per wave: up to four block ids
 constexpr int kPlanMagic = 0x504c0000;
 
 // The step's K/V rows written to position T_s - 1 of each sequence (the slot

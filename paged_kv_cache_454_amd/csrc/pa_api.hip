@@ -337,15 +337,13 @@ extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, flo
   return pa::launch_decode(p, stream);
 }
 
-extern "C" pa_status pa_decode_partitioned_fp8(
-    float *part_out, float *part_max, float *part_sum, const void *query,
+static pa_status decode_partitioned_fp8(
+    const char *fn, void *plan, uint32_t plan_epoch, float *part_out, float *part_max, float *part_sum, const void *query,
     const uint8_t *key_cache, const uint8_t *value_cache, const int32_t *block_tables,
     const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
     float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_parts,
     hipStream_t stream) {
-  pa::clear_error();
-  const char *fn = "pa_decode_partitioned_fp8";
   pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                        block_size, max_blocks_per_seq, num_blocks, scale, PA_BF16);
   if (st != PA_OK) return st;
@@ -382,7 +380,39 @@ extern "C" pa_status pa_decode_partitioned_fp8(
   p.kv_fp8 = 1;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.plan = plan;
+  p.plan_epoch = plan_epoch;
   return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_decode_partitioned_fp8(
+    float *part_out, float *part_max, float *part_sum, const void *query,
+    const uint8_t *key_cache, const uint8_t *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_parts,
+    hipStream_t stream) {
+  pa::clear_error();
+  return decode_partitioned_fp8("pa_decode_partitioned_fp8", nullptr, 0, part_out, part_max,
+                                part_sum, query, key_cache, value_cache, block_tables,
+                                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
+                                v_scale, partition_size, max_parts, stream);
+}
+
+extern "C" pa_status pa_decode_partitioned_fp8_planned(
+    float *part_out, float *part_max, float *part_sum, const void *query,
+    const uint8_t *key_cache, const uint8_t *value_cache, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_parts,
+    void *plan, uint32_t plan_epoch, hipStream_t stream) {
+  pa::clear_error();
+  return decode_partitioned_fp8("pa_decode_partitioned_fp8_planned", plan, plan_epoch, part_out,
+                                part_max, part_sum, query, key_cache, value_cache, block_tables,
+                                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
+                                v_scale, partition_size, max_parts, stream);
 }
 
 // Checks of a balanced call's scratch (caller-owned device memory, zero

@@ -205,6 +205,84 @@ __device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int
   bad_part = c_p * 4 + app * 2 + c_bad;
 }
 
+// ---- Plan cache (see DecodeParams::plan). A workgroup's slot is tagged with
+// the launch that wrote it; kind distinguishes kernels whose slots differ.
+typedef uint32_t plan_u32x4 __attribute__((ext_vector_type(4)));
+
+struct PlanSlot {
+  __amdgpu_buffer_rsrc_t r;  // this workgroup's slot (empty without a buffer)
+  plan_u32x4 tag;            // kind and mode, grid, batch size, partition size
+  bool use;                  // the slot holds this launch's plan
+};
+
+template <bool SPLIT>
+__device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind) {
+  PlanSlot ps;
+  ps.r = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t *>(p.plan) + (int64_t)blockIdx.x * kPlanWgBytes, (short)0,
+      p.plan ? kPlanWgBytes : 0, 0x00020000);
+  ps.tag = plan_u32x4{(uint32_t)kPlanMagic | kind | (SPLIT ? 1u : 0u) | (p.step ? 2u : 0u),
+                      gridDim.x, (uint32_t)p.num_seqs, (uint32_t)p.partition_size};
+  ps.use = false;
+  if (p.plan) {
+    const plan_u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanHdr, 0, 0);
+    const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanHdr + 16, 0, 0);
+    ps.use = __builtin_amdgcn_readfirstlane(h[0]) == ps.tag[0] &&
+             __builtin_amdgcn_readfirstlane(h[1]) == ps.tag[1] &&
+             __builtin_amdgcn_readfirstlane(h[2]) == ps.tag[2] &&
+             __builtin_amdgcn_readfirstlane(h[3]) == ps.tag[3] &&
+             __builtin_amdgcn_readfirstlane(e) == p.plan_epoch;
+  }
+  return ps;
+}
+
+// Wave 0: the workgroup's units, from the slot when it holds this launch's
+// plan (each checked, so that a plan made for other inputs can give wrong
+// numbers but never an access outside the caller's buffers), else planned
+// here and, with a buffer, stored with the tag for the launches after this
+// one. Every path issues the same stores (the unwanted ones go past
+// num_records and are dropped).
+template <bool SPLIT>
+__device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot &ps, int lane,
+                                          int *scr, int4 &my, int &my_bp, int &my_act) {
+  if (ps.use) {
+    const plan_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanUnits + 16 * lane, 0, 0);
+    const int bp = (int)__builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanBp + 4 * lane, 0, 0);
+    my = make_int4((int)u[0], (int)u[1], (int)u[2], (int)u[3]);
+    const int cap = p.max_blocks_per_seq * p.block_size;
+    my_act = bp >= 0 && my.x >= 0 && my.x < p.num_seqs && my.y >= 0 && my.y < p.num_kv_heads &&
+             my.z >= 0 && my.z <= my.w && my.w <= cap &&
+             (bp >> 2) < (SPLIT ? p.max_parts : 1) && (p.step || (bp & 2) == 0);
+    my_bp = my_act ? bp : 0;
+    if (!my_act) my = make_int4(0, 0, 0, 0);
+  } else {
+    plan_units<SPLIT>(p, lane, scr, my, my_bp, my_act);
+  }
+  if (p.plan) {
+    const int drop = ps.use ? kPlanWgBytes : 0;
+    __builtin_amdgcn_raw_buffer_store_b128(
+        plan_u32x4{(uint32_t)my.x, (uint32_t)my.y, (uint32_t)my.z, (uint32_t)my.w}, ps.r,
+        drop + kPlanUnits + 16 * lane, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(my_act ? (uint32_t)my_bp : 0xffffffffu, ps.r,
+                                          drop + kPlanBp + 4 * lane, 0, 0);
+    const uint32_t hv = lane < 4 ? ps.tag[lane & 3] : p.plan_epoch;
+    __builtin_amdgcn_raw_buffer_store_b32(hv, ps.r,
+                                          lane < 5 ? drop + kPlanHdr + 4 * lane : kPlanWgBytes,
+                                          0, 0);
+  }
+}
+
+// A wave's k-th stored block id (lane 0 stores; every lane holds the same).
+__device__ inline void plan_store_id(const PlanSlot &ps, int wave, int k, int lane, int id) {
+  const int drop = ps.use || lane != 0 ? kPlanWgBytes : 0;
+  __builtin_amdgcn_raw_buffer_store_b32((uint32_t)id, ps.r,
+                                        drop + kPlanIds + kPlanIdBytes * wave + 4 * k, 0, 0);
+}
+__device__ inline int plan_load_id(const PlanSlot &ps, int wave, int k) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanIds + kPlanIdBytes * wave + 4 * k,
+                                                   0, 0);
+}
+
 // Compute units of the current device (cached per device).
 inline int num_cus() {
   static int cached[64] = {0};

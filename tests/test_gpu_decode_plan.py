@@ -159,3 +159,36 @@ def test_plan_not_applicable_shapes():
             assert np.array_equal(a, b)
         torch.cuda.synchronize()
         assert int(buf.sum()) == 0
+
+
+def _fp8_records(t, case, P, ks, vs, plan=None, epoch=0):
+    po, pm, ps = _parts(case, P)
+    pa.pa_decode_partitioned_fp8(po, pm, ps, t["query"], t["key_cache"], t["value_cache"],
+                                 t["block_tables"], t["context_lens"], case.scale, ks, vs, P,
+                                 plan=plan, plan_epoch=epoch)
+    return [G.bits(x) for x in (po, pm, ps)]
+
+
+@pytest.mark.parametrize("preset", ["mixed", "long"])
+def test_planned_fp8_bitexact(preset):
+    """The FP8 kernel with a plan buffer: the same bits as without (the first
+    launch of the epoch plans, the next read); slots a BF16 launch wrote under
+    the same epoch are replanned, not read."""
+    print(f"[plan] fp8 preset={preset}", flush=True)
+    from tests.test_gpu_fp8 import _fp8_case, _write
+    import bench
+    ks, vs = bench.FP8_SCALES[preset]
+    case = inputs.preset_case(preset, seed=0)
+    t, _, _ = _fp8_case(case, ks, vs)
+    _write(t, ks, vs)
+    P = G.bench_partitions()[1][preset]
+    want = _fp8_records(t, case, P, ks, vs)
+    plan = pa.decode_plan_buffer()
+    for _ in range(2):
+        for a, b in zip(want, _fp8_records(t, case, P, ks, vs, plan, 4)):
+            assert np.array_equal(a, b)
+    tb = G.to_dev(case)
+    G.write(tb)
+    _partitioned(tb, case, G.bench_partitions()[0][preset], plan, 4)    # BF16 slots
+    for a, b in zip(want, _fp8_records(t, case, P, ks, vs, plan, 4)):
+        assert np.array_equal(a, b)
