@@ -442,8 +442,9 @@ def read_ceiling(dev, seed, reps=5):
 
 def loop_leg(seed, steps, dev):
     """Continuous-batching decode loop (``DecodeLoop``): 64 batch slots, 16
-    layers of the mixed workload's shape (24/4 heads, d 256, block 16,
-    1024-token partitions). Prompts are drawn log-uniform in [16, 8192] like
+    layers of the mixed workload's shape (24/4 heads, d 256, block 16, the
+    mixed workload's partition size), each layer one pa_decode_step call
+    sharing the step's plan. Prompts are drawn log-uniform in [16, 8192] like
     the mixed workload, generation lengths uniform in [16, 128]; a finished
     request's slot is refilled at once (its prompt K/V written into all 16
     layers). Times `steps` whole iterations (native allocator step, batch
@@ -457,7 +458,8 @@ def loop_leg(seed, steps, dev):
 
     from paged_kv_cache_454_amd import inputs
     from paged_kv_cache_454_amd.decode_loop import DecodeLoop
-    slots, layers, hq, hkv, d, bs, P = 64, 16, 24, 4, 256, 16, 1024
+    slots, layers, hq, hkv, d, bs = 64, 16, 24, 4, 256, 16
+    P = DEFAULT_PARTITION["mixed"]
     maxc = 8192 + 512
     nb = slots * (maxc // bs) + 64
     rng = np.random.default_rng(seed + 1)
@@ -502,8 +504,8 @@ def loop_leg(seed, steps, dev):
         del loop
         torch.cuda.empty_cache()
     return {
-        "workload": "continuous-batching decode loop: 64 slots, 16 layers, 24/4 heads, d 256, "
-                    "bs 16, P 1024, prompts log-uniform [16, 8192], generation uniform [16, 128]",
+        "workload": f"continuous-batching decode loop: 64 slots, 16 layers, 24/4 heads, d 256, "
+                    f"bs 16, P {P}, prompts log-uniform [16, 8192], generation uniform [16, 128]",
         "steps": steps, **res,
     }
 

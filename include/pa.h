@@ -316,13 +316,17 @@ pa_status pa_decode_step(void *out, float *part_out, float *part_max, float *par
  * workgroup, each tagged with the launch that wrote it: entry point kind,
  * grid, num_seqs, partition_size and the caller's plan_epoch. A launch given
  * a buffer and an epoch reads its slot when the tag matches, and otherwise
- * plans as usual and writes the slot. The caller's contract: one epoch value
- * names one set of context_lens, block_tables and sizes (take a new epoch
- * whenever they change, e.g. once per decode step); with a stale epoch the
- * outputs are wrong (the kernel still never accesses memory outside the
- * caller's buffers). Launches that share a buffer must run in order (one
- * stream). Where the matrix-core kernel does not take the shape the buffer is
- * not used. Results are bit for bit those of the calls without a plan.
+ * plans as usual and writes the slot. An epoch with bit 31 set always plans
+ * and stores the slots under the epoch without that bit: a step's first
+ * layer can pass E | 0x80000000 and the later layers E, the same values every
+ * step (so a captured graph replays correctly). The caller's contract: a
+ * launch that reads (bit 31 clear) finds slots written for the same
+ * context_lens, block_tables and sizes (take a new epoch whenever they
+ * change, or refresh with bit 31); with a stale plan the outputs are wrong
+ * (the kernel still never accesses memory outside the caller's buffers).
+ * Launches that share a buffer must run in order (one stream). Where the
+ * matrix-core kernel does not take the shape the buffer is not used. Results
+ * are bit for bit those of the calls without a plan.
  */
 size_t pa_decode_plan_bytes(void);
 

@@ -224,7 +224,9 @@ __device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind) {
   ps.tag = plan_u32x4{(uint32_t)kPlanMagic | kind | (SPLIT ? 1u : 0u) | (p.step ? 2u : 0u),
                       gridDim.x, (uint32_t)p.num_seqs, (uint32_t)p.partition_size};
   ps.use = false;
-  if (p.plan) {
+  // Bit 31 of the epoch asks for a fresh plan, stored under the epoch
+  // without that bit.
+  if (p.plan && !(p.plan_epoch & 0x80000000u)) {
     const plan_u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanHdr, 0, 0);
     const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanHdr + 16, 0, 0);
     ps.use = __builtin_amdgcn_readfirstlane(h[0]) == ps.tag[0] &&
@@ -265,7 +267,7 @@ __device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot 
         drop + kPlanUnits + 16 * lane, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(my_act ? (uint32_t)my_bp : 0xffffffffu, ps.r,
                                           drop + kPlanBp + 4 * lane, 0, 0);
-    const uint32_t hv = lane < 4 ? ps.tag[lane & 3] : p.plan_epoch;
+    const uint32_t hv = lane < 4 ? ps.tag[lane & 3] : (p.plan_epoch & 0x7fffffffu);
     __builtin_amdgcn_raw_buffer_store_b32(hv, ps.r,
                                           lane < 5 ? drop + kPlanHdr + 4 * lane : kPlanWgBytes,
                                           0, 0);

@@ -7,21 +7,26 @@ its slowest member; section 2: blocks are handed out as tokens arrive).
 A fixed number of batch slots each hold one running request or nothing.
 One step:
   * host: one native call (``BlockAllocator.step``) appends a token to every
-    running request and exports their block-table rows, context lengths and
-    the new tokens' slots; idle slots get length 0 and slot -1;
-  * device, for every layer: the slot-mapped write of the step's new K/V
-    rows (``pa_reshape_and_cache``), split decode (``pa_decode_partitioned``)
-    and the log-sum-exp merge (``pa_reduce``);
+    running request and exports their block-table rows and context lengths;
+    idle slots get length 0 (the new token's slot is the last position's,
+    which the device call reads from the table);
+  * device, for every layer: one ``pa_decode_step`` call, which writes the
+    step's new K/V rows at each request's newest position and runs the split
+    decode and the log-sum-exp merge (two launches). The first layer's call
+    deals the batch's work to the compute units and stores that plan; the
+    other layers read it (the same lengths and tables serve every layer);
   * host: requests that reached their length release their blocks.
 Admitting a request allocates its prompt and writes the prompt's K/V rows
 for every layer (eager launches).
 
-All device buffers of a step (queries, new K/V rows, slots, tables, lengths,
-partition workspace, outputs) live at fixed addresses, and the kernels take
+All device buffers of a step (queries, new K/V rows, tables, lengths,
+partition workspace, plan, outputs) live at fixed addresses, and the kernels take
 the batch composition from device memory (idle rows are empty contexts and
 skipped slots), so the device part of a step can be captured once as a HIP
-graph and replayed: each step then costs one native allocator call, three
-host-to-device copies and one graph launch.
+graph and replayed: each step then costs one native allocator call, two
+host-to-device copies and one graph launch. The plan is refreshed by the
+first layer of every step, eager or replayed, so it never outlives the batch
+it was made for.
 
 This is host orchestration only; every step of the attention path runs in
 the library's kernels.
@@ -32,7 +37,12 @@ import math
 import numpy as np
 import torch
 
-from .binding import (BlockAllocator, pa_decode_partitioned, pa_reduce, pa_reshape_and_cache)
+from .binding import BlockAllocator, decode_plan_buffer, pa_decode_step, pa_reshape_and_cache
+
+# Plan epoch of the loop's launches; the first layer of a step adds bit 31
+# (plan afresh and store), the others read that plan.
+_EPOCH = 1
+_REFRESH = 0x80000000
 
 
 class DecodeLoop:
@@ -59,10 +69,8 @@ class DecodeLoop:
         self.new_k = torch.zeros((L, S, self.hkv, self.d), dtype=bf, device=self.dev)
         self.new_v = torch.zeros((L, S, self.hkv, self.d), dtype=bf, device=self.dev)
         # Batch description, host (pinned) and device.
-        self.h_slot = torch.full((S,), -1, dtype=torch.int64).pin_memory()
         self.h_table = torch.full((S, self.max_blocks), -1, dtype=torch.int32).pin_memory()
         self.h_lens = torch.zeros((S,), dtype=torch.int32).pin_memory()
-        self.d_slot = torch.full((S,), -1, dtype=torch.int64, device=self.dev)
         self.d_table = torch.full((S, self.max_blocks), -1, dtype=torch.int32, device=self.dev)
         self.d_lens = torch.zeros((S,), dtype=torch.int32, device=self.dev)
         # Partition workspace (shared by the layers, which run in order) and outputs.
@@ -72,6 +80,7 @@ class DecodeLoop:
                                     device=self.dev)
         self.part_sum = torch.empty_like(self.part_max)
         self.out = torch.empty((L, S, self.hq, self.d), dtype=torch.float32, device=self.dev)
+        self.plan = decode_plan_buffer(self.dev)
         self.scale = 1.0 / math.sqrt(self.d)
         # slot -> [seq_id, tokens still to generate]
         self.running = [None] * S
@@ -107,30 +116,26 @@ class DecodeLoop:
     # -------------------------------------------------------------------- step
     def _device_step(self):
         for l, (kc, vc) in enumerate(self.pools):
-            pa_reshape_and_cache(self.new_k[l], self.new_v[l], kc, vc, self.d_slot)
-            pa_decode_partitioned(self.part_out, self.part_max, self.part_sum, self.query[l], kc,
-                                  vc, self.d_table, self.d_lens, self.scale, self.partition_size)
-            pa_reduce(self.out[l], self.part_out, self.part_max, self.part_sum, self.d_lens,
-                      self.partition_size)
+            pa_decode_step(self.out[l], self.query[l], self.new_k[l], self.new_v[l], kc, vc,
+                           self.d_table, self.d_lens, self.scale, self.partition_size,
+                           self.part_out, self.part_max, self.part_sum, plan=self.plan,
+                           plan_epoch=_EPOCH | (_REFRESH if l == 0 else 0))
 
     def step(self):
         """One iteration. Returns the (slot, seq_id) pairs that ran; their
         attention outputs are in self.out[:, slot] until the next step."""
         act = [(i, r[0]) for i, r in enumerate(self.running) if r is not None]
         ids = [sid for _, sid in act]
-        slots, table, lens = self.alloc.step(ids, np.ones(len(ids), dtype=np.int32),
+        _, table, lens = self.alloc.step(ids, np.ones(len(ids), dtype=np.int32),
                                              self.max_blocks)
         if self._copied is not None:
             self._copied.synchronize()   # the pinned buffers are free again
-        hs, ht, hl = self.h_slot.numpy(), self.h_table.numpy(), self.h_lens.numpy()
-        hs.fill(-1)
+        ht, hl = self.h_table.numpy(), self.h_lens.numpy()
         ht.fill(-1)
         hl.fill(0)
         rows = [i for i, _ in act]
-        hs[rows] = slots
         ht[rows] = table
         hl[rows] = lens
-        self.d_slot.copy_(self.h_slot, non_blocking=True)
         self.d_table.copy_(self.h_table, non_blocking=True)
         self.d_lens.copy_(self.h_lens, non_blocking=True)
         self._copied = torch.cuda.Event()

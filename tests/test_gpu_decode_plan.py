@@ -192,3 +192,19 @@ def test_planned_fp8_bitexact(preset):
     _partitioned(tb, case, G.bench_partitions()[0][preset], plan, 4)    # BF16 slots
     for a, b in zip(want, _fp8_records(t, case, P, ks, vs, plan, 4)):
         assert np.array_equal(a, b)
+
+
+def test_refresh_bit_replans_under_a_fixed_epoch():
+    """Bit 31 of the epoch plans afresh and stores the slots under the epoch
+    without it: three growing batches through one buffer with the same two
+    epoch values every step (refresh on the first call, read on the next)."""
+    plan = pa.decode_plan_buffer()
+    lens = np.array(EDGE_LENS)
+    for k in range(3):
+        case = inputs.decode_case(lens + 7 * k, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2,
+                                  seed=60 + k)
+        base, _ = _step(case, 512)
+        got0, _ = _step(case, 512, plan, 5 | 0x80000000)
+        got1, _ = _step(case, 512, plan, 5)
+        assert np.array_equal(G.bits(base), G.bits(got0)), k
+        assert np.array_equal(G.bits(base), G.bits(got1)), k
