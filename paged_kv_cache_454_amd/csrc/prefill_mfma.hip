@@ -168,8 +168,40 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // blocks see more tokens: launch them first.
   const int SK = p.num_seqs * p.num_kv_heads;
   const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
-  const int sk = xcd + NXCD * (slot / row_blocks);
-  if (sk >= SK) return;
+  const int q_round = slot / row_blocks;  // the XCD's q_round-th pair
+  int sk;
+  if (SK <= 64) {
+    // Pairs are dealt by cost: every wave ranks the pairs by their K/V tiles
+    // summed over the row blocks (largest first, ties by index) and deals
+    // them to the XCDs in snake order (round q goes 0..7 when even, 7..0
+    // when odd), so each XCD gets an equal count and nearly equal work, and
+    // each XCD starts its largest pairs first.
+    int cost = -1;
+    if (lane < SK) {
+      const int si = lane / p.num_kv_heads;
+      const int ni = p.query_start_loc[si + 1] - p.query_start_loc[si];
+      const int Ti = p.context_lens[si];
+      const int nr = ni * G;
+      cost = 0;
+      if (ni > 0 && Ti >= ni && (int64_t)Ti <= (int64_t)p.max_blocks_per_seq * p.block_size)
+        for (int b = 0; b * ROWS < nr; ++b) {
+          const int lim = Ti - ni + (min(b * ROWS + ROWS, nr) - 1) / G + 1;
+          cost += (lim + KT - 1) / KT;
+        }
+    }
+    int rank = 0;
+    for (int k = 0; k < 64; ++k) {
+      const int ck = __builtin_amdgcn_readlane(cost, k);
+      rank += ck > cost || (ck == cost && k < lane);
+    }
+    const int want = NXCD * q_round + ((q_round & 1) ? NXCD - 1 - xcd : xcd);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < SK && rank == want);
+    if (hit == 0) return;
+    sk = __builtin_ctzll(hit);
+  } else {
+    sk = xcd + NXCD * q_round;
+    if (sk >= SK) return;
+  }
   const int rb = row_blocks - 1 - slot % row_blocks;
   const int kvh = sk % p.num_kv_heads;
   const int s = sk / p.num_kv_heads;
