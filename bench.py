@@ -114,6 +114,9 @@ def parse():
                          "pa_reshape_and_cache, then the decode and pa_reduce (default: per "
                          "workload, the faster measured). Split and whole modes only; the other "
                          "form is timed too, as ms_per_step_other")
+    ap.add_argument("--compare-step", type=int, default=1,
+                    help="also time the other step form (0: only the chosen one, e.g. for "
+                         "counter runs that should see one form's launches)")
     ap.add_argument("--side-decode", type=int, default=1,
                     help="with the mixed workload, also time the long-context and uniform "
                          "decode workloads (0: skip)")
@@ -620,7 +623,8 @@ MODE_KERNEL = {"split": "pa_decode_partitioned_planned",
 DEFAULT_STEP = {"mixed": "fused", "long": "fused", "uniform": "fused"}
 
 
-def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_form="fused"):
+def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_form="fused",
+               compare=True):
     """One decode workload at full size: K timed steps (per pool set: the
     slot write of the step's new K/V, pa_decode_partitioned at partition
     size P, pa_reduce; as one pa_decode_step call when step_form is "fused")
@@ -713,9 +717,10 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
     fusable = mode in ("split", "whole")
     if not fusable:
         step_form = "calls"
+    compare = compare and fusable
     main = step_fused if step_form == "fused" else step_calls
     other = step_calls if step_form == "fused" else step_fused
-    if fusable:
+    if compare:
         # The two forms alternate, three timings each, medians reported: the
         # clocks settle over the first timings, so back-to-back single
         # timings would favour whichever form runs second.
@@ -782,7 +787,7 @@ def main():
     fp8_P = (args.fp8_partition_size or FP8_DEFAULT_PARTITION[W]) if args.fp8 else None
     mode = args.mode or DEFAULT_MODE[W]
     main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P, mode,
-                          args.step or DEFAULT_STEP[W])
+                          args.step or DEFAULT_STEP[W], bool(args.compare_step))
 
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
@@ -814,7 +819,7 @@ def main():
             f2 = FP8_DEFAULT_PARTITION[w2] if (args.fp8 and w2 == "long") else None
             result[w2] = decode_leg(w2, DEFAULT_PARTITION[w2], args.steps, args.warmup, dev,
                                     args.seed, f2, DEFAULT_MODE[w2],
-                                    args.step or DEFAULT_STEP[w2])
+                                    args.step or DEFAULT_STEP[w2], bool(args.compare_step))
     if args.prefill_reps > 0:
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
