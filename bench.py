@@ -219,23 +219,27 @@ def timed_launches(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
-def decode_launch_ms(launch, nlayers, reps, stream):
+def decode_launch_ms(launch, nlayers, reps, stream, min_launches=16):
     """Mean duration (ms) of one decode launch: each repetition runs the
-    decode of every layer back to back between two HIP events on the stream
-    the kernels are launched on. The host enqueues a launch much faster than
-    the GPU runs it, so the queue stays ahead and the events see the
-    kernels (and the gaps between them), not the host's submission time."""
+    layers' decodes back to back, cycling through the layers for at least
+    min_launches launches, between two HIP events on the stream the kernels
+    are launched on. The host enqueues a launch much faster than the GPU
+    runs it, so the queue stays ahead and the events see the kernels (and
+    the gaps between them), not the host's submission time; the latency
+    from the first event to the first kernel is spread over the pair's
+    launches (with three launches per pair it added about 3 us to each)."""
     import torch
+    n = nlayers * max(1, -(-min_launches // nlayers))
     pairs = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for li in range(nlayers):
-            launch(li)
+        for i in range(n):
+            launch(i % nlayers)
         b.record(stream)
         pairs.append((a, b))
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / nlayers
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / n
 
 
 def prefill_leg(seed, reps, dev):
