@@ -219,15 +219,16 @@ def timed_launches(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
-def decode_launch_ms(launch, nlayers, reps, stream, min_launches=16):
+def decode_launch_ms(launch, nlayers, reps, stream, min_launches=48):
     """Mean duration (ms) of one decode launch: each repetition runs the
     layers' decodes back to back, cycling through the layers for at least
     min_launches launches, between two HIP events on the stream the kernels
     are launched on. The host enqueues a launch much faster than the GPU
     runs it, so the queue stays ahead and the events see the kernels (and
-    the gaps between them), not the host's submission time; the latency
-    from the first event to the first kernel is spread over the pair's
-    launches (with three launches per pair it added about 3 us to each)."""
+    the gaps between them), not the host's submission time. In a kernel
+    trace the GPU idles up to 10 us where one event pair ends and the next
+    begins, against about 0.5 us between launches inside a pair; with three
+    launches per pair that added about 3 us to each."""
     import torch
     n = nlayers * max(1, -(-min_launches // nlayers))
     pairs = []
