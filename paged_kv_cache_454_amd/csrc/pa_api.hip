@@ -290,18 +290,15 @@ extern "C" size_t pa_partition_workspace_bytes(int32_t num_seqs, int32_t num_q_h
   return n * (size_t)head_dim * sizeof(float) + 2 * n * sizeof(float);
 }
 
-extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, float *part_sum,
-                                           const void *query, const void *key_cache,
-                                           const void *value_cache, const int32_t *block_tables,
-                                           const int32_t *context_lens, int32_t num_seqs,
-                                           int32_t num_q_heads, int32_t num_kv_heads,
-                                           int32_t head_dim, int32_t block_size,
-                                           int32_t max_blocks_per_seq, int32_t num_blocks,
-                                           float scale, int32_t partition_size,
-                                           int32_t max_parts, pa_dtype kv_dtype,
-                                           hipStream_t stream) {
-  pa::clear_error();
-  const char *fn = "pa_decode_partitioned";
+static pa_status decode_partitioned(const char *fn, void *plan, uint32_t plan_epoch,
+                                   float *part_out, float *part_max, float *part_sum,
+                                   const void *query, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, float scale, int32_t partition_size,
+                                   int32_t max_parts, pa_dtype kv_dtype, hipStream_t stream) {
   pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                        block_size, max_blocks_per_seq, num_blocks, scale,
                                        kv_dtype);
@@ -334,7 +331,26 @@ extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, flo
   p.partition_size = partition_size;
   p.max_parts = max_parts;
   p.kv_bf16 = kv_dtype == PA_BF16;
+  p.plan = plan;
+  p.plan_epoch = plan_epoch;
   return pa::launch_decode(p, stream);
+}
+
+extern "C" pa_status pa_decode_partitioned(float *part_out, float *part_max, float *part_sum,
+                                           const void *query, const void *key_cache,
+                                           const void *value_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                                           float scale, int32_t partition_size,
+                                           int32_t max_parts, pa_dtype kv_dtype,
+                                           hipStream_t stream) {
+  pa::clear_error();
+  return decode_partitioned("pa_decode_partitioned", nullptr, 0, part_out, part_max, part_sum,
+                            query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                            num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            num_blocks, scale, partition_size, max_parts, kv_dtype, stream);
 }
 
 static pa_status decode_partitioned_fp8(
@@ -704,42 +720,11 @@ extern "C" pa_status pa_decode_partitioned_planned(
     int32_t partition_size, int32_t max_parts, pa_dtype kv_dtype, void *plan,
     uint32_t plan_epoch, hipStream_t stream) {
   pa::clear_error();
-  const char *fn = "pa_decode_partitioned_planned";
-  pa_status st = check_attention_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                       block_size, max_blocks_per_seq, num_blocks, scale,
-                                       kv_dtype);
-  if (st != PA_OK) return st;
-  if (partition_size < 16 || partition_size % block_size != 0)
-    return pa::fail(PA_EINVAL, "%s: partition_size=%d must be >= 16 and a multiple of block_size=%d",
-                    fn, partition_size, block_size);
-  if (max_parts <= 0) return pa::fail(PA_EINVAL, "%s: max_parts=%d must be > 0", fn, max_parts);
-  if (num_seqs == 0) return PA_OK;
-  if (!part_out || !part_max || !part_sum || !query || !key_cache || !value_cache ||
-      !block_tables || !context_lens)
-    return pa::fail(PA_EINVAL, "%s: null pointer argument", fn);
-  pa::DecodeParams p{};
-  p.query = query;
-  p.key_cache = key_cache;
-  p.value_cache = value_cache;
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
-  p.part_out = part_out;
-  p.part_max = part_max;
-  p.part_sum = part_sum;
-  p.num_seqs = num_seqs;
-  p.num_q_heads = num_q_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.head_dim = head_dim;
-  p.block_size = block_size;
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.num_blocks = num_blocks;
-  p.scale = scale;
-  p.partition_size = partition_size;
-  p.max_parts = max_parts;
-  p.kv_bf16 = kv_dtype == PA_BF16;
-  p.plan = plan;
-  p.plan_epoch = plan_epoch;
-  return pa::launch_decode(p, stream);
+  return decode_partitioned("pa_decode_partitioned_planned", plan, plan_epoch, part_out,
+                            part_max, part_sum, query, key_cache, value_cache, block_tables,
+                            context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
+                            max_parts, kv_dtype, stream);
 }
 
 extern "C" pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
