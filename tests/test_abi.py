@@ -25,7 +25,9 @@ def test_header_declares_the_boundary():
               "pa_prefill_chunk", "pa_alloc_create", "pa_alloc_append", "pa_alloc_free",
               "pa_alloc_block_table", "pa_last_error", "pa_reshape_and_cache_fp8",
               "pa_decode_fp8", "pa_decode_partitioned_fp8", "pa_swap_blocks",
-              "pa_alloc_swap_out", "pa_alloc_swap_in", "pa_alloc_set_host_pool"]:
+              "pa_alloc_swap_out", "pa_alloc_swap_in", "pa_alloc_set_host_pool",
+              "pa_decode_step", "pa_decode_plan_bytes", "pa_decode_partitioned_planned",
+              "pa_decode_partitioned_fp8_planned", "pa_decode_balanced"]:
         assert n in names
 
 
@@ -96,6 +98,43 @@ def test_partitioned_and_reduce_reject_bad_partitions():
     assert st == _lib.PA_EINVAL
     assert lib.pa_partition_workspace_bytes(4, 24, 256, 64) == 4 * 24 * 64 * (256 + 2) * 4
     assert lib.pa_partition_workspace_bytes(0, 24, 256, 64) == 0
+
+
+def _step(lib, **kw):
+    a = dict(out=NULL, po=NULL, pm=NULL, ps=NULL, q=NULL, k=NULL, v=NULL, kc=NULL, vc=NULL,
+             bt=NULL, cl=NULL, num_seqs=2, hq=24, hkv=4, d=256, bs=16, maxb=8, nb=100,
+             scale=0.0625, P=512, mp=4, kv=1, od=0, plan=NULL, epoch=0)
+    a.update(kw)
+    return lib.pa_decode_step(a["out"], a["po"], a["pm"], a["ps"], a["q"], a["k"], a["v"],
+                              a["kc"], a["vc"], a["bt"], a["cl"], a["num_seqs"], a["hq"],
+                              a["hkv"], a["d"], a["bs"], a["maxb"], a["nb"], a["scale"], a["P"],
+                              a["mp"], a["kv"], a["od"], a["plan"], a["epoch"], NULL)
+
+
+def test_decode_step_rejects_bad_arguments():
+    lib = _lib.lib()
+    assert _step(lib, P=48, bs=32) == _lib.PA_EINVAL               # not a multiple of bs
+    assert b"partition_size" in lib.pa_last_error()
+    assert _step(lib, P=8) == _lib.PA_EINVAL                       # under 16
+    assert _step(lib, mp=0) == _lib.PA_EINVAL
+    assert _step(lib, hq=25) == _lib.PA_EINVAL
+    assert _step(lib, d=96) == _lib.PA_EUNSUPPORTED
+    assert _step(lib, od=5) == _lib.PA_EINVAL
+    assert _step(lib) == _lib.PA_EINVAL and b"null" in lib.pa_last_error()
+    assert _step(lib, P=0, mp=0) == _lib.PA_EINVAL                 # single pass, null pointers
+    assert _step(lib, num_seqs=0) == _lib.PA_OK                    # nothing to do
+
+
+def test_planned_calls_reject_bad_arguments():
+    lib = _lib.lib()
+    st = lib.pa_decode_partitioned_planned(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 2, 24,
+                                           4, 256, 32, 8, 100, 0.0625, 48, 4, 1, NULL, 1, NULL)
+    assert st == _lib.PA_EINVAL and b"pa_decode_partitioned_planned" in lib.pa_last_error()
+    st = lib.pa_decode_partitioned_fp8_planned(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 2,
+                                               24, 4, 256, 16, 8, 100, 0.0625, 0.0, 1.0, 512, 4,
+                                               NULL, 1, NULL)
+    assert st == _lib.PA_EINVAL                                     # zero k_scale
+    assert b"pa_decode_partitioned_fp8_planned" in lib.pa_last_error()
 
 
 def test_prefill_rejects_bad_arguments():
