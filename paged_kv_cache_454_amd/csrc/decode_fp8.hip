@@ -169,7 +169,7 @@ void decode_fp8_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
   __shared__ int ubadpart[MAXU];   // part * 4 + bad (no step tokens here)
-  __shared__ uint32_t act_lds[2];
+  __shared__ uint32_t act_lds[3];  // active-unit mask, and whether the plan slot is used
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -184,7 +184,6 @@ void decode_fp8_kernel(DecodeParams p) {
   int pre_id[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) pre_id[k] = plan_load_id(ps, wave, k);
-  const bool use_plan = ps.use;
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
@@ -195,12 +194,17 @@ void decode_fp8_kernel(DecodeParams p) {
     if (lane == 0) {
       act_lds[0] = (uint32_t)m;
       act_lds[1] = (uint32_t)(m >> 32);
+      act_lds[2] = ps.use ? 1u : 0u;
     }
   }
   __syncthreads();
   const uint64_t act_mask =
       (uint64_t)__builtin_amdgcn_readfirstlane(act_lds[0]) |
       ((uint64_t)__builtin_amdgcn_readfirstlane(act_lds[1]) << 32);
+  // Wave 0's reading of the slot decides for the workgroup: it may rewrite
+  // the slot's tag before a later wave reads it, and each wave's own ids in
+  // the slot are as the launch that wrote the tag left them.
+  const bool use_plan = __builtin_amdgcn_readfirstlane(act_lds[2]) != 0;
   if (act_mask == 0) return;  // uniform for the workgroup
 
   const int bs = p.block_size;
@@ -358,10 +362,10 @@ void decode_fp8_kernel(DecodeParams p) {
     load_v(vb, d1, nv_b, bad_b);
     advance();
     dn2 = make_desc();
-    plan_store_id(ps, wave, 0, lane, d0.blk0);
-    plan_store_id(ps, wave, 1, lane, d0.blk1);
-    plan_store_id(ps, wave, 2, lane, d1.blk0);
-    plan_store_id(ps, wave, 3, lane, d1.blk1);
+    plan_store_id(ps, use_plan, wave, 0, lane, d0.blk0);
+    plan_store_id(ps, use_plan, wave, 1, lane, d0.blk1);
+    plan_store_id(ps, use_plan, wave, 2, lane, d1.blk0);
+    plan_store_id(ps, use_plan, wave, 3, lane, d1.blk1);
   }
 
   auto stage_queries = [&](uint64_t mask) {

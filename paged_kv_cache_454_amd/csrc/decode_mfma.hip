@@ -164,7 +164,7 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint4 qs[C::NQ][G][QROW];
   __shared__ int4 uinfo[MAXU];     // (s, h, lo, hi)
   __shared__ int ubadpart[MAXU];   // part * 4 + 2 * append + bad
-  __shared__ uint32_t act_lds[2];
+  __shared__ uint32_t act_lds[3];  // active-unit mask, and whether the plan slot is used
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,7 +179,6 @@ void decode_mfma_kernel(DecodeParams p) {
   // this launch; otherwise planned here and stored.
   const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindMfma);
   const int pre_id0 = plan_load_id(ps, wave, 0), pre_id1 = plan_load_id(ps, wave, 1);
-  const bool use_plan = ps.use;
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
@@ -190,12 +189,17 @@ void decode_mfma_kernel(DecodeParams p) {
     if (lane == 0) {
       act_lds[0] = (uint32_t)m;
       act_lds[1] = (uint32_t)(m >> 32);
+      act_lds[2] = ps.use ? 1u : 0u;
     }
   }
   __syncthreads();
   const uint64_t act_mask =
       (uint64_t)__builtin_amdgcn_readfirstlane(act_lds[0]) |
       ((uint64_t)__builtin_amdgcn_readfirstlane(act_lds[1]) << 32);
+  // Wave 0's reading of the slot decides for the workgroup: it may rewrite
+  // the slot's tag before a later wave reads it, and each wave's own ids in
+  // the slot are as the launch that wrote the tag left them.
+  const bool use_plan = __builtin_amdgcn_readfirstlane(act_lds[2]) != 0;
   if (act_mask == 0) return;  // uniform for the workgroup
 
   const int bs = p.block_size;
@@ -340,8 +344,8 @@ void decode_mfma_kernel(DecodeParams p) {
     dn2 = make_desc();
     // The wave's first two ids, stored for the launches after this one
     // unless they came from the slot (dropped stores otherwise).
-    plan_store_id(ps, wave, 0, lane, d0.blk);
-    plan_store_id(ps, wave, 1, lane, d1.blk);
+    plan_store_id(ps, use_plan, wave, 0, lane, d0.blk);
+    plan_store_id(ps, use_plan, wave, 1, lane, d1.blk);
   }
 
   auto stage_queries = [&](uint64_t mask) {

@@ -275,8 +275,11 @@ __device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot 
 }
 
 // A wave's k-th stored block id (lane 0 stores; every lane holds the same).
-__device__ inline void plan_store_id(const PlanSlot &ps, int wave, int k, int lane, int id) {
-  const int drop = ps.use || lane != 0 ? kPlanWgBytes : 0;
+// The store is dropped when the workgroup read its slot (use: wave 0's
+// decision, shared through LDS).
+__device__ inline void plan_store_id(const PlanSlot &ps, bool use, int wave, int k, int lane,
+                                     int id) {
+  const int drop = use || lane != 0 ? kPlanWgBytes : 0;
   __builtin_amdgcn_raw_buffer_store_b32((uint32_t)id, ps.r,
                                         drop + kPlanIds + kPlanIdBytes * wave + 4 * k, 0, 0);
 }
