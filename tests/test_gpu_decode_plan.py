@@ -208,3 +208,34 @@ def test_refresh_bit_replans_under_a_fixed_epoch():
         got1, _ = _step(case, 512, plan, 5)
         assert np.array_equal(G.bits(base), G.bits(got0)), k
         assert np.array_equal(G.bits(base), G.bits(got1)), k
+
+
+def test_plan_buffer_across_random_batches():
+    """One plan buffer driven through 12 random batches (sizes, lengths,
+    partition sizes, step or plain calls), each decoded three times: a fresh
+    epoch, the same epoch again, and a refresh under it; every output is
+    bit for bit the unplanned call's."""
+    rng = np.random.default_rng(23)
+    plan = pa.decode_plan_buffer()
+    epoch = 1000
+    for k in range(12):
+        S = int(rng.integers(70, 200))
+        lens = [int(x) for x in rng.integers(1, 4000, S)]
+        P = int(rng.choice([256, 512, 1024]))
+        step = bool(rng.integers(0, 2))
+        case = inputs.decode_case(lens, 24, 4, 256, 16, dtype="bf16", pool_factor=1.1,
+                                  seed=100 + k)
+        print(f"[plan] random batch {k}: S={S} P={P} step={step}", flush=True)
+        epoch += 1
+        if step:
+            base, _ = _step(case, P)
+            for e in (epoch, epoch, epoch | 0x80000000):
+                got, _ = _step(case, P, plan, e)
+                assert np.array_equal(G.bits(base), G.bits(got)), (k, e)
+        else:
+            t = G.to_dev(case)
+            G.write(t)
+            want = _partitioned(t, case, P)
+            for e in (epoch, epoch, epoch | 0x80000000):
+                for a, b in zip(want, _partitioned(t, case, P, plan, e)):
+                    assert np.array_equal(a, b), (k, e)
