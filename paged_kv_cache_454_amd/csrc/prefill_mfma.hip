@@ -65,6 +65,15 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// l + lo + hi of a pair of BF16 weights in one instruction (a dot product
+// with (1, 1)): the row sum uses exactly the rounded weights the matrix
+// products use.
+__device__ __forceinline__ float row_sum_add(uint32_t pair, float l) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, l, false);
+}
+
 // s_waitcnt immediates: vmcnt(n) with the other counters left at their maxima.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kVmcnt8 = waitcnt_vm(8);
@@ -341,26 +350,38 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint8_t *vl = cur[1];
     const int t0 = it * KT;
 
-    // S^T (32 tokens x 32 rows).
-    f32x16 s0 = {};
+    // S^T (32 tokens x 32 rows). The K fragments are read three steps
+    // ahead of their products, in a fixed order.
+    f32x16 s0;
     const uint8_t *krow = kl + tile_off(tok_of(l32), 8 * half);
+    uint4 kf[4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s0 = mfma(*reinterpret_cast<const uint4 *>(krow + 32 * k), qf[k], s0);
+    for (int k = 0; k < 3; ++k) kf[k] = *reinterpret_cast<const uint4 *>(krow + 32 * k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k + 3 < 16) kf[(k + 3) & 3] = *reinterpret_cast<const uint4 *>(krow + 32 * (k + 3));
+      s0 = k == 0 ? mfma(kf[0], qf[0], f32x16{}) : mfma(kf[k & 3], qf[k], s0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4.
     float z[16];
-    float mx = -INFINITY;
-    const bool full = t0 + KT <= wave_min_lim;  // uniform: no token of the tile is masked
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = s0[e] * sl2;
-      if (full) {
-        z[e] = v;
-      } else {
+    for (int e = 0; e < 16; ++e) z[e] = s0[e] * sl2;
+    if (t0 + KT > wave_min_lim) {  // uniform: some token of the tile is masked for this wave
+      // Only the tiles on the causal diagonal (and past short contexts)
+      // take this branch; the empty statement keeps it a branch instead of
+      // selects that every tile would pay for.
+      asm volatile("");
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
         const int tok = t0 + tok_of(8 * (e >> 2) + 4 * half + (e & 3));
-        z[e] = tok < limit ? v : -INFINITY;
+        z[e] = tok < limit ? z[e] : -INFINITY;
       }
-      mx = fmaxf(mx, z[e]);
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
     mx = other_half_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
       const float mn = fmaxf(m, mx);
@@ -383,7 +404,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         const float pa = fast_exp2(z[8 * c + 2 * u] - m);
         const float pb = fast_exp2(z[8 * c + 2 * u + 1] - m);
         w4[u] = bf16_pair(pa, pb);
-        l += __uint_as_float(w4[u] << 16) + __uint_as_float(w4[u] & 0xffff0000u);
+        l = row_sum_add(w4[u], l);
       }
       pw[c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
