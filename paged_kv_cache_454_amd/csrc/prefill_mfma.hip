@@ -97,11 +97,12 @@ __device__ __forceinline__ int tok_of(int m) {
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // (i % 4) of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.
-__device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint64_t tr_read(const lds_u8 *p) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_v4 *)((__attribute__((address_space(3))) uint8_t *)lds_byte_ptr));
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4 *)p);
   return __builtin_bit_cast(uint64_t, v);
 }
 
@@ -113,21 +114,25 @@ __device__ __forceinline__ uint64_t tr_read(const uint8_t *lds_byte_ptr) {
 // a barrier) before any wave reads the stage they fill; vector memory
 // operations complete in order, so the compiler's own waits for other loads
 // stay correct (they only become stricter).
-// M0 (the LDS address of the load) is saved and restored inside the
-// statement, and the one wait state between writing M0 and the load that
-// reads it is an explicit s_nop.
+// M0 (the LDS address of the load) is declared clobbered, so the compiler
+// sets it again wherever it needs it; the one wait state between writing
+// M0 and the load that reads it is an explicit s_nop.
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_load16(u32x4v rsrc, uint32_t lds_addr, uint32_t voffset) {
-  uint32_t saved_m0;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
       : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-      : "memory");
+      : "memory", "m0");
+}
+
+// 16 bytes from LDS.
+__device__ __forceinline__ uint4 lds_read16(const lds_u8 *p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(__attribute__((address_space(3))) const u32x4 *)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Buffer resource over [base, base + bytes): raw buffer, no stride, the
@@ -161,6 +166,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // it+3 do not write the stage being read, and does not wait for them.
   typedef uint8_t Stage[2][TILE_BYTES];  // [K|V][token pair]
   __shared__ __attribute__((aligned(16))) Stage stage0, stage1, stage2, stage3;
+  // The stages by LDS address (constants), so that no generic pointer has
+  // to be converted in the loop.
+  lds_u8 *const st0 = (lds_u8 *)&stage0[0][0];
+  lds_u8 *const st1 = (lds_u8 *)&stage1[0][0];
+  lds_u8 *const st2 = (lds_u8 *)&stage2[0][0];
+  lds_u8 *const st3 = (lds_u8 *)&stage3[0][0];
   static_assert(STAGES == 4, "the ring is four named stages");
   __shared__ int tab[MAX_TABLE];
 
@@ -276,7 +287,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // resource of each instruction covers just the valid rows of its token pair
   // (zero bytes past the context or for an invalid block id), so the LDS
   // receives zeros there without a memory access.
-  auto issue_tile = [&](int it, Stage &dst) {
+  // Tiles are issued in order, so each of the wave's two token pairs keeps a
+  // cursor (table index, token within the block) that moves on by one tile
+  // per issue: no division per load.
+  const int q_kt = KT / bs, r_kt = KT % bs;
+  int cur_b[KT / 2 / WAVES], cur_r[KT / 2 / WAVES];
+#pragma unroll
+  for (int i = 0; i < KT / 2 / WAVES; ++i) {
+    const int tok0 = 2 * (wave * (KT / 2 / WAVES) + i);
+    cur_b[i] = tok0 / bs;
+    cur_r[i] = tok0 - cur_b[i] * bs;
+  }
+  auto issue_tile = [&](int it, lds_u8 *dst) {
     const int t_base = it * KT;
 #pragma unroll
     for (int i = 0; i < KT / 2 / WAVES; ++i) {
@@ -284,17 +306,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       const int tok0 = t_base + 2 * pi;
       int nv = wg_limit - tok0;
       nv = __builtin_amdgcn_readfirstlane(nv < 0 ? 0 : (nv > 2 ? 2 : nv));
-      int blk = nv > 0 ? tab[tok0 / bs] : 0;
-      blk = __builtin_amdgcn_readfirstlane(blk);
-      if (blk < 0 || blk >= nb) {
+      // The table index stays inside the staged table; past the context the
+      // id read is not used (nv = 0).
+      int blk = __builtin_amdgcn_readfirstlane(tab[cur_b[i] < MAX_TABLE ? cur_b[i] : MAX_TABLE - 1]);
+      if (nv == 0 || (uint32_t)blk >= (uint32_t)nb) {  // also blk < 0
         nv = 0;
         blk = 0;
       }
-      const int64_t off = (int64_t)blk * block_stride + (int64_t)(tok0 % bs) * D;
-      const uint32_t kdst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)&dst[0][pi * PAIR])));
-      const uint32_t vdst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)&dst[1][pi * PAIR])));
+      const int64_t off = (int64_t)blk * block_stride + (int64_t)cur_r[i] * D;
+      cur_r[i] += r_kt;
+      cur_b[i] += q_kt;
+      if (cur_r[i] >= bs) {
+        cur_r[i] -= bs;
+        cur_b[i] += 1;
+      }
+      const uint32_t kdst = (uint32_t)(uintptr_t)(dst + pi * PAIR);
+      const uint32_t vdst = (uint32_t)(uintptr_t)(dst + TILE_BYTES + pi * PAIR);
       lds_load16(raw_rsrc(kpool + off, nv * D * 2), kdst, lane * 16);
       lds_load16(raw_rsrc(vpool + off, nv * D * 2), vdst, lane * 16);
     }
@@ -307,6 +334,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m = kNoMax, l = 0.f;
   const float sl2 = p.scale * kLog2e;
+  const bool pos_scale = sl2 > 0.f;
+  const float zscale = pos_scale ? sl2 : 1.f;  // what the kept scores still need
 
   // Lane roles in the transpose reads of V (A operand of O^T): the lane is
   // k = lane % 16 of a 16-lane group; it supplies the address of token
@@ -334,40 +363,48 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // leave: a wait for them inside the loop would also wait for every tile
   // load in flight.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  issue_tile(0, stage0);
-  issue_tile(1, stage1);
-  issue_tile(2, stage2);
+  issue_tile(0, st0);
+  issue_tile(1, st1);
+  issue_tile(2, st2);
 
   // One tile: `cur` holds tile it, `nxt` (the stage tile it-1 used) receives
   // tile it+3.
-  auto step = [&](int it, Stage &cur, Stage &nxt) {
+  auto step = [&](int it, const lds_u8 *cur, lds_u8 *nxt) {
     // This wave's loads for tile it are complete once only the two later
     // tiles' are outstanding (4 instructions per tile per wave).
     __builtin_amdgcn_s_waitcnt(kVmcnt8);
     __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
     issue_tile(it + STAGES - 1, nxt);
-    const uint8_t *kl = cur[0];
-    const uint8_t *vl = cur[1];
+    const lds_u8 *kl = cur;
+    const lds_u8 *vl = cur + TILE_BYTES;
     const int t0 = it * KT;
 
     // S^T (32 tokens x 32 rows). The K fragments are read three steps
     // ahead of their products, in a fixed order.
     f32x16 s0;
-    const uint8_t *krow = kl + tile_off(tok_of(l32), 8 * half);
+    const lds_u8 *krow = kl + tile_off(tok_of(l32), 8 * half);
     uint4 kf[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) kf[k] = *reinterpret_cast<const uint4 *>(krow + 32 * k);
+    for (int k = 0; k < 3; ++k) kf[k] = lds_read16(krow + 32 * k);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      if (k + 3 < 16) kf[(k + 3) & 3] = *reinterpret_cast<const uint4 *>(krow + 32 * (k + 3));
+      if (k + 3 < 16) kf[(k + 3) & 3] = lds_read16(krow + 32 * (k + 3));
       s0 = k == 0 ? mfma(kf[0], qf[0], f32x16{}) : mfma(kf[k & 3], qf[k], s0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4.
+    // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4. The
+    // scores stay unscaled here (for a positive scale the max commutes with
+    // the scaling, and rounding is monotone, so the scaled max is exactly
+    // the max of the scaled scores); the scale enters the exponent's fma.
     float z[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = s0[e] * sl2;
+    for (int e = 0; e < 16; ++e) z[e] = s0[e];
+    if (!pos_scale) {
+      asm volatile("");
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[e] *= sl2;
+    }
     if (t0 + KT > wave_min_lim) {  // uniform: some token of the tile is masked for this wave
       // Only the tiles on the causal diagonal (and past short contexts)
       // take this branch; the empty statement keeps it a branch instead of
@@ -382,7 +419,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, z[e]);
-    mx = other_half_max(mx);
+    mx = other_half_max(mx) * zscale;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
       const float mn = fmaxf(m, mx);
       const float a = fast_exp2(m - mn);
@@ -401,8 +438,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       uint32_t w4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float pa = fast_exp2(z[8 * c + 2 * u] - m);
-        const float pb = fast_exp2(z[8 * c + 2 * u + 1] - m);
+        const float pa = fast_exp2(__builtin_fmaf(z[8 * c + 2 * u], zscale, -m));
+        const float pb = fast_exp2(__builtin_fmaf(z[8 * c + 2 * u + 1], zscale, -m));
         w4[u] = bf16_pair(pa, pb);
         l = row_sum_add(w4[u], l);
       }
@@ -411,7 +448,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // O^T (32 channels x 32 rows per dt) += V^T . P^T. The A operand comes
     // from the row-major V tile through two transpose reads whose token
     // order matches the weights'.
-    const uint8_t *vbase = vl + vpair * PAIR + 2 * vd0;
+    const lds_u8 *vbase = vl + vpair * PAIR + 2 * vd0;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
@@ -427,13 +464,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   };
 
   for (int it = 0; it < ntiles; it += STAGES) {
-    step(it, stage0, stage3);
+    step(it, st0, st3);
     if (it + 1 >= ntiles) break;
-    step(it + 1, stage1, stage0);
+    step(it + 1, st1, st0);
     if (it + 2 >= ntiles) break;
-    step(it + 2, stage2, stage1);
+    step(it + 2, st2, st1);
     if (it + 3 >= ntiles) break;
-    step(it + 3, stage3, stage2);
+    step(it + 3, st3, st2);
   }
   // The loads issued for the three tiles past the end (empty, but they still
   // write LDS) finish before any wave of the workgroup ends.
