@@ -12,8 +12,8 @@
 //
 // Per 32-token K/V tile (K and V gathered through the block table straight
 // into an LDS ring of 4 tiles by buffer-to-LDS loads, 3 tiles in flight,
-// token pairs 1 KiB + 16 B apart; one barrier per tile, after each wave's
-// own wait for its loads of that tile):
+// token pairs 1 KiB + 16 B (K) or + 32 B (V) apart; one barrier per tile,
+// after each wave's own wait for its loads of that tile):
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (M = 32 tokens, N = 32
 //    rows, K = 16 channels; 16 steps over head_dim). In the accumulator
 //    layout each lane holds one query row (lane % 32) and 16 of the tile's
@@ -43,8 +43,10 @@ constexpr int WAVES = 8;                // two per SIMD
 constexpr int ROWS = WAVES * 32;        // query rows per workgroup
 constexpr int KT = 32;                  // tokens per K/V tile
 constexpr int STAGES = 4;               // K/V tiles in the LDS ring (3 in flight)
-constexpr int PAIR = 1040;              // bytes per token pair in LDS: 2 x 512 + 16 of bank offset
-constexpr int TILE_BYTES = (KT / 2) * PAIR;  // one K (or V) tile
+constexpr int PAIR = 1040;              // K tile: bytes per token pair in LDS, 2 x 512 + 16
+constexpr int PAIR_V = 1056;            // V tile: bytes per token pair in LDS, 2 x 512 + 32
+constexpr int TILE_K = (KT / 2) * PAIR;    // one K tile
+constexpr int TILE_V = (KT / 2) * PAIR_V;  // one V tile
 constexpr int MAX_TABLE = 2048;         // block ids staged in LDS
 constexpr int NXCD = 8;                 // XCDs (dies) the workgroups are dealt to
 constexpr float kLazy = 8.f;
@@ -78,10 +80,14 @@ __device__ __forceinline__ float row_sum_add(uint32_t pair, float l) {
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kVmcnt8 = waitcnt_vm(8);
 
-// LDS byte offset of channel ch of token row t in a K or V tile: token pairs
-// are 1 KiB apart plus 16 bytes, so the 32 token rows of an operand read fall
-// on distinct bank groups (two rows per group, the minimum for 512 bytes) and
-// every fragment address is a lane base plus an immediate.
+// LDS byte offset of channel ch of token row t in a K tile: token pairs are
+// 1 KiB apart plus 16 bytes, so the 16 lanes a 16-byte read serves per cycle
+// (64 banks of 4 bytes) address 16 different 16-byte bank slots, and every
+// fragment address is a lane base plus an immediate. V tiles use the same
+// layout with pairs 1 KiB + 32 bytes apart: the transposed 8-byte reads serve
+// 32 lanes per cycle, whose addresses step by two pairs, and two pairs must
+// then be 64 bytes of banks apart for the 32 to cover all 64 banks once
+// (with 16 bytes, lanes two pairs apart met on the same banks).
 __device__ __forceinline__ int tile_off(int t, int ch) { return (t >> 1) * PAIR + (t & 1) * 512 + ch * 2; }
 
 // Token of the tile in slot m (0..31) of the S^T rows and of the P.V sums.
@@ -164,14 +170,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // STAGES, so every buffer-to-LDS load and every LDS read names its stage
   // statically: the compiler can then tell that the loads issued for tile
   // it+3 do not write the stage being read, and does not wait for them.
-  typedef uint8_t Stage[2][TILE_BYTES];  // [K|V][token pair]
+  typedef uint8_t Stage[TILE_K + TILE_V];  // K tile, then V tile
   __shared__ __attribute__((aligned(16))) Stage stage0, stage1, stage2, stage3;
   // The stages by LDS address (constants), so that no generic pointer has
   // to be converted in the loop.
-  lds_u8 *const st0 = (lds_u8 *)&stage0[0][0];
-  lds_u8 *const st1 = (lds_u8 *)&stage1[0][0];
-  lds_u8 *const st2 = (lds_u8 *)&stage2[0][0];
-  lds_u8 *const st3 = (lds_u8 *)&stage3[0][0];
+  lds_u8 *const st0 = (lds_u8 *)&stage0[0];
+  lds_u8 *const st1 = (lds_u8 *)&stage1[0];
+  lds_u8 *const st2 = (lds_u8 *)&stage2[0];
+  lds_u8 *const st3 = (lds_u8 *)&stage3[0];
   static_assert(STAGES == 4, "the ring is four named stages");
   __shared__ int tab[MAX_TABLE];
 
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         cur_b[i] += 1;
       }
       const uint32_t kdst = (uint32_t)(uintptr_t)(dst + pi * PAIR);
-      const uint32_t vdst = (uint32_t)(uintptr_t)(dst + TILE_BYTES + pi * PAIR);
+      const uint32_t vdst = (uint32_t)(uintptr_t)(dst + TILE_K + pi * PAIR_V);
       lds_load16(raw_rsrc(kpool + off, nv * D * 2), kdst, lane * 16);
       lds_load16(raw_rsrc(vpool + off, nv * D * 2), vdst, lane * 16);
     }
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
     issue_tile(it + STAGES - 1, nxt);
     const lds_u8 *kl = cur;
-    const lds_u8 *vl = cur + TILE_BYTES;
+    const lds_u8 *vl = cur + TILE_K;
     const int t0 = it * KT;
 
     // S^T (32 tokens x 32 rows). The K fragments are read three steps
@@ -448,14 +454,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // O^T (32 channels x 32 rows per dt) += V^T . P^T. The A operand comes
     // from the row-major V tile through two transpose reads whose token
     // order matches the weights'.
-    const lds_u8 *vbase = vl + vpair * PAIR + 2 * vd0;
+    const lds_u8 *vbase = vl + vpair * PAIR_V + 2 * vd0;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // row c of pair vpair, and of pair vpair + 8
         const uint64_t va = tr_read(vbase + c * 512 + dt * 64);
-        const uint64_t vb = tr_read(vbase + c * 512 + 8 * PAIR + dt * 64);
+        const uint64_t vb = tr_read(vbase + c * 512 + 8 * PAIR_V + dt * 64);
         const uint4 a = make_uint4((uint32_t)va, (uint32_t)(va >> 32), (uint32_t)vb,
                                    (uint32_t)(vb >> 32));
         o[dt] = mfma(a, pw[c], o[dt]);
