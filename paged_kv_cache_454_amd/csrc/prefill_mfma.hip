@@ -380,7 +380,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // tiles' are outstanding (4 instructions per tile per wave).
     __builtin_amdgcn_s_waitcnt(kVmcnt8);
     __syncthreads();  // every wave's loads for tile it are in LDS; stage it-1 is free
-    issue_tile(it + STAGES - 1, nxt);
     const lds_u8 *kl = cur;
     const lds_u8 *vl = cur + TILE_K;
     const int t0 = it * KT;
@@ -399,6 +398,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       s0 = k == 0 ? mfma(kf[0], qf[0], f32x16{}) : mfma(kf[k & 3], qf[k], s0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The loads of tile it+3 (into the stage tile it-1 left) go out here,
+    // after the S products, and not right after the barrier, where every
+    // wave of the workgroup would queue its address work on the compute
+    // unit's one scalar unit while the matrix cores wait.
+    issue_tile(it + STAGES - 1, nxt);
     // Element e of the accumulator is slot 8*(e/4) + 4*half + e%4. The
     // scores stay unscaled here (for a positive scale the max commutes with
     // the scaling, and rounding is monotone, so the scaled max is exactly
