@@ -359,12 +359,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // zeros. Every step then issues the same 4 instructions per wave and the
   // compiler's wait counts stay exact (a conditional issue would make it
   // wait for every load before each LDS read).
-  // Waves 0-3 (one per SIMD) win the SIMD's issue arbitration: after each
-  // barrier they take the matrix core first, and their softmax then runs on
-  // the vector unit while the SIMD's other wave multiplies, instead of both
-  // waves of a SIMD doing the same phase at the same time.
-  if (wave < WAVES / 2) __builtin_amdgcn_s_setprio(1);
-
   // The query fragments must be in registers before the first tile loads
   // leave: a wait for them inside the loop would also wait for every tile
   // load in flight.
