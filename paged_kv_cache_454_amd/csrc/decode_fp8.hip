@@ -180,10 +180,10 @@ void decode_fp8_kernel(DecodeParams p) {
   const int S = p.num_seqs, H = p.num_kv_heads, HQ = p.num_q_heads;
   // With a plan buffer: the slot, this wave's first four block ids and (wave
   // 0) the units, loaded together when the slot's tag names this launch.
-  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindFp8);
+  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindFp8, wave, wave == 0);
   int pre_id[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) pre_id[k] = plan_load_id(ps, wave, k);
+  for (int k = 0; k < 4; ++k) pre_id[k] = (int)ps.ids[k];
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;

@@ -177,8 +177,8 @@ void decode_mfma_kernel(DecodeParams p) {
   // With a plan buffer: this workgroup's slot, this wave's first two block
   // ids and (wave 0) the units, loaded together when the slot's tag names
   // this launch; otherwise planned here and stored.
-  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindMfma);
-  const int pre_id0 = plan_load_id(ps, wave, 0), pre_id1 = plan_load_id(ps, wave, 1);
+  const PlanSlot ps = plan_slot<SPLIT>(p, kPlanKindMfma, wave, wave == 0);
+  const int pre_id0 = (int)ps.ids[0], pre_id1 = (int)ps.ids[1];
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;

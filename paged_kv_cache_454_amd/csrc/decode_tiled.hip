@@ -126,6 +126,30 @@ void decode_tiled_kernel(DecodeParams p) {
   const int seq = rest % p.num_seqs;
   const int part = rest / p.num_seqs;
 
+  // Everything the first tiles need is requested at once, before any of it
+  // is waited for: the context length, the block ids of this wave's first
+  // three tiles and the group's query rows. The ids are looked up before the
+  // length is known (a table index past the row is clamped into it; ids of
+  // tiles past the context are never used), and the queries go to registers
+  // and reach LDS after the first tile's loads have been issued.
+  const int bs = p.block_size;
+  typedef __attribute__((address_space(4))) const int32_t cint32;
+  cint32 *tab = (cint32 *)(p.block_tables + (int64_t)seq * p.max_blocks_per_seq);
+  const int64_t lo0 = p.partition_size > 0 ? (int64_t)part * p.partition_size : 0;
+  auto early_id = [&](int j) -> int {
+    const int64_t e = (lo0 + (int64_t)(wave + j * NW) * TILE) / bs;
+    return tab[e < p.max_blocks_per_seq ? e : p.max_blocks_per_seq - 1];
+  };
+  const int eid0 = early_id(0), eid1 = early_id(1), eid2 = early_id(2);
+  static_assert(G * 32 <= NW * 64, "one 16-byte query piece per thread");
+  const int64_t qrow = (int64_t)seq * p.num_q_heads + (int64_t)kvh * G;
+  uint4 qpiece = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < G * 32) {
+    const vec16 v = load16(reinterpret_cast<const uint16_t *>(p.query) +
+                           (qrow + threadIdx.x / 32) * D + (threadIdx.x % 32) * 8);
+    qpiece = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+  }
+
   int T = p.context_lens[seq];
   T = T < 0 ? 0 : T;
   bool bad = false;
@@ -147,17 +171,6 @@ void decode_tiled_kernel(DecodeParams p) {
   // the lane's 8 channels of one head at a time, which keeps 4*G registers
   // free for the K/V pipeline.
   __shared__ uint4 qs[G][32];
-  const int64_t qrow = (int64_t)seq * p.num_q_heads + (int64_t)kvh * G;
-  for (int i = threadIdx.x; i < G * 32; i += NW * 64) {
-    const vec16 v = load16(reinterpret_cast<const uint16_t *>(p.query) + (qrow + i / 32) * D +
-                           (i % 32) * 8);
-    qs[i / 32][i % 32] = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-  }
-  // The query must have landed before the K/V pipeline starts: otherwise the
-  // compiler may sink these loads behind the first tile's, and the wait for
-  // them would drain every prefetched tile on each iteration.
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
 
   float acc[G][8];
 #pragma unroll
@@ -172,8 +185,6 @@ void decode_tiled_kernel(DecodeParams p) {
   }
 
   const float sl2 = p.scale * kLog2e;
-  const int bs = p.block_size;
-  const int32_t *table = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
   const int64_t head_stride = (int64_t)bs * D;
   const int64_t block_stride = head_stride * p.num_kv_heads;
   const uint16_t *kpool = reinterpret_cast<const uint16_t *>(p.key_cache) + kvh * head_stride;
@@ -182,8 +193,6 @@ void decode_tiled_kernel(DecodeParams p) {
   // This wave's tiles are kk = wave + j * NW, j < nj. Block ids come through
   // the scalar cache (uniform per wavefront) one iteration ahead of the
   // loads that need them, so no vector-memory wait is spent on the table.
-  typedef __attribute__((address_space(4))) const int32_t cint32;
-  cint32 *tab = (cint32 *)(table);
   const int nj = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
   auto block_of = [&](int j) -> int {
     const int kk = wave + j * NW;
@@ -338,12 +347,16 @@ void decode_tiled_kernel(DecodeParams p) {
   // Q.K and its V right after (reusing the registers this tile's K just
   // freed), so 8-16 KiB per wavefront are always in flight.
   vec16 ka[LOADS], va[LOADS], kb[LOADS], vb[LOADS];
-  int blk1 = block_of(1), blk2 = block_of(2);
+  int blk1 = wave + NW < ntiles ? eid1 : 0, blk2 = wave + 2 * NW < ntiles ? eid2 : 0;
   {
-    const int blk0 = block_of(0);
+    const int blk0 = wave < ntiles ? eid0 : 0;
     load8(ka, tile_rsrc(0, blk0, kpool));
     load8(va, tile_rsrc(0, blk0, vpool));
   }
+  // The queries reach LDS behind the first tile's loads (their wait leaves
+  // those in flight) and must be there before the first Q.K.
+  if (threadIdx.x < G * 32) qs[threadIdx.x / 32][threadIdx.x % 32] = qpiece;
+  __syncthreads();
   for (int j = 0; j < nj; j += 2) {
     const int blk3 = block_of(j + 3), blk4 = block_of(j + 4);
     load8(kb, tile_rsrc(j + 1, blk1, kpool));

@@ -213,10 +213,19 @@ struct PlanSlot {
   __amdgpu_buffer_rsrc_t r;  // this workgroup's slot (empty without a buffer)
   plan_u32x4 tag;            // kind and mode, grid, batch size, partition size
   bool use;                  // the slot holds this launch's plan
+  plan_u32x4 ids;            // the wave's stored block ids (up to four)
+  plan_u32x4 unit;           // with_units: the lane's stored unit ...
+  uint32_t bp;               // ... and its partition * 4 + flags word
 };
 
+// The wave's stored block ids and (with_units, wave 0) the lane's unit
+// entry are loaded together with the header, before the tag is checked, so
+// that a launch reading its plan waits for one round trip, not two. They
+// lie inside the slot, so the loads are harmless when the tag turns out not
+// to match (the values are then not used).
 template <bool SPLIT>
-__device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind) {
+__device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind, int wave,
+                                     bool with_units) {
   PlanSlot ps;
   ps.r = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<uint8_t *>(p.plan) + (int64_t)blockIdx.x * kPlanWgBytes, (short)0,
@@ -224,11 +233,20 @@ __device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind) {
   ps.tag = plan_u32x4{(uint32_t)kPlanMagic | kind | (SPLIT ? 1u : 0u) | (p.step ? 2u : 0u),
                       gridDim.x, (uint32_t)p.num_seqs, (uint32_t)p.partition_size};
   ps.use = false;
+  ps.ids = plan_u32x4{0u, 0u, 0u, 0u};
+  ps.unit = plan_u32x4{0u, 0u, 0u, 0u};
+  ps.bp = 0xffffffffu;
   // Bit 31 of the epoch asks for a fresh plan, stored under the epoch
   // without that bit.
   if (p.plan && !(p.plan_epoch & 0x80000000u)) {
     const plan_u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanHdr, 0, 0);
     const uint32_t e = __builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanHdr + 16, 0, 0);
+    ps.ids = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanIds + kPlanIdBytes * wave, 0, 0);
+    if (with_units) {
+      const int lane = threadIdx.x & 63;
+      ps.unit = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanUnits + 16 * lane, 0, 0);
+      ps.bp = __builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanBp + 4 * lane, 0, 0);
+    }
     ps.use = __builtin_amdgcn_readfirstlane(h[0]) == ps.tag[0] &&
              __builtin_amdgcn_readfirstlane(h[1]) == ps.tag[1] &&
              __builtin_amdgcn_readfirstlane(h[2]) == ps.tag[2] &&
@@ -238,8 +256,8 @@ __device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind) {
   return ps;
 }
 
-// Wave 0: the workgroup's units, from the slot when it holds this launch's
-// plan (each checked, so that a plan made for other inputs can give wrong
+// Wave 0: the workgroup's units, from the slot (loaded by plan_slot with
+// with_units) when it holds this launch's plan (each checked, so that a plan made for other inputs can give wrong
 // numbers but never an access outside the caller's buffers), else planned
 // here and, with a buffer, stored with the tag for the launches after this
 // one. Every path issues the same stores (the unwanted ones go past
@@ -248,8 +266,8 @@ template <bool SPLIT>
 __device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot &ps, int lane,
                                           int *scr, int4 &my, int &my_bp, int &my_act) {
   if (ps.use) {
-    const plan_u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(ps.r, kPlanUnits + 16 * lane, 0, 0);
-    const int bp = (int)__builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanBp + 4 * lane, 0, 0);
+    const plan_u32x4 u = ps.unit;
+    const int bp = (int)ps.bp;
     my = make_int4((int)u[0], (int)u[1], (int)u[2], (int)u[3]);
     const int cap = p.max_blocks_per_seq * p.block_size;
     my_act = bp >= 0 && my.x >= 0 && my.x < p.num_seqs && my.y >= 0 && my.y < p.num_kv_heads &&
@@ -282,10 +300,6 @@ __device__ inline void plan_store_id(const PlanSlot &ps, bool use, int wave, int
   const int drop = use || lane != 0 ? kPlanWgBytes : 0;
   __builtin_amdgcn_raw_buffer_store_b32((uint32_t)id, ps.r,
                                         drop + kPlanIds + kPlanIdBytes * wave + 4 * k, 0, 0);
-}
-__device__ inline int plan_load_id(const PlanSlot &ps, int wave, int k) {
-  return (int)__builtin_amdgcn_raw_buffer_load_b32(ps.r, kPlanIds + kPlanIdBytes * wave + 4 * k,
-                                                   0, 0);
 }
 
 // Compute units of the current device (cached per device).

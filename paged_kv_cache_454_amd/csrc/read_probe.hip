@@ -7,9 +7,11 @@
 // With the identity order it is a plain streaming read; with a random
 // permutation it is the gather pattern of decode without its arithmetic.
 //
-// Four wavefronts per workgroup, one workgroup per CU; global wave w reads
+// Eight wavefronts per workgroup, one workgroup per CU; global wave w reads
 // blocks order[w], order[w + W], ... (W = all waves), each through a ring of
-// two blocks in flight. Every word read is folded into a per-lane XOR, which
+// two blocks in flight. Measured on MI355X over random 8 KiB blocks, eight
+// waves per CU read 13 % faster than four (with the same or twice the bytes
+// in flight), and four blocks in flight per wave are slower than two. Every word read is folded into a per-lane XOR, which
 // is stored at the end (the data must be consumed, and the XOR of all sinks
 // equals the XOR of all words read, which the tests check).
 #include "launch.h"
@@ -19,7 +21,7 @@
 namespace pa {
 namespace {
 
-constexpr int kProbeWaves = 4;
+constexpr int kProbeWaves = 8;
 constexpr int kProbeBlock = 8192;
 typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
 
