@@ -63,6 +63,7 @@ using namespace persist;
 constexpr int D = 256;      // head_dim
 constexpr int TILE = 16;    // tokens per tile
 constexpr int NW = 8;       // wavefronts per workgroup (two per SIMD)
+static_assert(NW == persist::kPlanWaves, "the planner's unit costs count 8 waves");
 constexpr int KL = 8;       // 16-byte K loads per lane per tile
 constexpr int VL = 8;       // 16-byte V loads per lane per tile
 constexpr int VROW = 544;   // bytes per token row of a wave's LDS V buffer
@@ -182,7 +183,7 @@ void decode_mfma_kernel(DecodeParams p) {
   if (wave == 0) {
     int4 my{0, 0, 0, 0};
     int my_bp = 0, my_act = 0;
-    plan_or_load_units<SPLIT>(p, ps, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
+    plan_or_load_units<SPLIT, TILE>(p, ps, lane, reinterpret_cast<int *>(red), my, my_bp, my_act);
     uinfo[lane] = my;
     ubadpart[lane] = my_bp;
     const uint64_t m = __builtin_amdgcn_ballot_w64(my_act != 0);

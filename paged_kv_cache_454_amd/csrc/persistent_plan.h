@@ -205,6 +205,279 @@ __device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int
   bad_part = c_p * 4 + app * 2 + c_bad;
 }
 
+// ---- Longest-first deal.
+//
+// The snake deal above balances unit counts, not work: on a batch whose
+// full partitions all cost the same and whose last partitions vary, its
+// second round lands small units on workgroups that already hold a full
+// one. plan_units_lpt deals the same units longest-first instead: each unit,
+// largest first, goes to the workgroup with the least work so far (ties to
+// the lowest index). A unit's cost is the stream positions it gives wave 0
+// (the most of any wave): ceil(tiles / NWAVES), padded to even. The result
+// does not depend on the deal (a unit's arithmetic is the same on every
+// workgroup); only the balance does. It is made by launches that store
+// their plan (a step's later layers read it) and only where it can beat
+// the snake deal.
+//
+// Units of equal cost are dealt at once: with costs c, the greedy choice is
+// the least (load + i c, workgroup) "slot" among all workgroups' free slots,
+// so n units of cost c take the n least slots in that order. A binary search
+// on the slot value finds the level of the n-th slot, and the workgroups
+// just below it, lowest index first, take the rest. Within a cost class the
+// units are numbered by sequence, then partition, then head, and a
+// workgroup's slots map to those numbers by their rank among all slots.
+constexpr int kPlanWaves = 8;       // wavefronts of the persistent kernels
+constexpr int kLptMaxGroups = 256;  // workgroups one wavefront tracks (4 per lane)
+
+// Wave-wide reductions (every lane receives the result; all 64 lanes must
+// be active): rotations by 8, 4, 2 and 1 inside each 16-lane row, then the
+// four rows combined with two lane swaps. Integer DPP and swaps, no LDS.
+template <int CTRL>
+__device__ __forceinline__ int lpt_dpp(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce(int x, Op op) {
+  x = op(x, lpt_dpp<0x128>(x));
+  x = op(x, lpt_dpp<0x124>(x));
+  x = op(x, lpt_dpp<0x122>(x));
+  x = op(x, lpt_dpp<0x121>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = op((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  // The same in every lane: readfirstlane lets the compiler keep it, and the
+  // control flow that depends on it, scalar.
+  return __builtin_amdgcn_readfirstlane(op((int)b[0], (int)b[1]));
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  return wave_reduce(x, [](int u, int v) { return u + v; });
+}
+__device__ __forceinline__ int wave_max(int x) {
+  return wave_reduce(x, [](int u, int v) { return u > v ? u : v; });
+}
+__device__ __forceinline__ int wave_min(int x) {
+  return wave_reduce(x, [](int u, int v) { return u < v ? u : v; });
+}
+
+// Inclusive prefix sum over the wave's lanes (all 64 active): shifts by 1,
+// 2, 4 and 8 inside each 16-lane row, then the totals of the rows below
+// added on.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
+// Stream positions of wave 0 for a unit of nt tiles, halved (costs are even).
+__device__ __forceinline__ int lpt_half_cost(int nt) {
+  const int c = (nt + kPlanWaves - 1) / kPlanWaves;
+  const int pc = c + (c & 1);
+  return pc > 2 ? pc / 2 : 1;  // an empty unit still merges and stores
+}
+
+// Division by a class's cost c (uniform) through a multiply-high by
+// m = ceil(2^32 / c) (c > 1): exact for t * c < 2^32, which the planner's
+// bounds guarantee.
+struct LptDiv {
+  int c;
+  uint32_t m;
+  __device__ __forceinline__ int floor_div(int t) const {
+    return c == 1 ? t : (int)__umulhi((uint32_t)t, m);
+  }
+};
+__device__ __forceinline__ LptDiv lpt_div(int c) {
+  return LptDiv{c, c > 1 ? 0xffffffffu / (uint32_t)c + 1u : 0u};
+}
+// Slots of one workgroup with load L below level v: ceil((v - L) / c)
+// (selects, no branches).
+__device__ __forceinline__ int lpt_slots_below(int v, int L, const LptDiv &d) {
+  const int t = v - L;
+  const int q = d.floor_div(t > 0 ? t - 1 : 0) + 1;
+  return t > 0 ? q : 0;
+}
+// Whether the workgroup has a slot exactly at level v.
+__device__ __forceinline__ int lpt_slot_at(int v, int L, const LptDiv &d) {
+  const int t = v - L;
+  const int tt = t > 0 ? t : 0;
+  return (t >= 0) & (d.floor_div(tt) * d.c == tt);
+}
+
+// Deals this workgroup's units longest-first (one per lane, as plan_units).
+// Returns false, leaving the outputs alone, where it does not apply: more
+// than 64 sequences, more than kLptMaxGroups workgroups, or a deal that
+// would give a workgroup more than MAXU units. Run by one wavefront, with
+// the same inputs and so the same deal on every workgroup.
+// scr: 192 ints of this wave's LDS (prologue scratch).
+template <bool SPLIT, int TILE_TOKENS>
+__device__ inline bool plan_units_lpt(const DecodeParams &p, int lane, int *scr, int4 &unit,
+                                      int &bad_part, int &active) {
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  const int NB = gridDim.x, b0 = blockIdx.x;
+  if (S > 64 || NB > kLptMaxGroups) return false;
+  const int P = SPLIT ? p.partition_size : 0;
+  const SeqParts sp = seq_parts<SPLIT>(p, lane);
+  const int live_seq = lane < S;
+
+  // This lane's sequence: its partitions fall into at most three cost
+  // classes: full ones, the last full one when it holds the step's token,
+  // and the last partial one (single pass: the whole context).
+  int nfa = 0, lastapp = 0, cf = 0, cfa = 0, cp = 0;
+  if (live_seq) {
+    if (SPLIT) {
+      lastapp = p.step && !sp.partial && sp.nfull > 0 && sp.T > 0 && !sp.bad;
+      nfa = sp.nfull - lastapp;
+      if (nfa > 0) cf = lpt_half_cost(P / TILE_TOKENS);
+      if (lastapp) cfa = lpt_half_cost((P - 1 + TILE_TOKENS - 1) / TILE_TOKENS + 1);
+      if (sp.partial) {
+        const int z = sp.T - sp.nfull * P;
+        const int app = p.step && sp.T > 0 && !sp.bad;
+        cp = lpt_half_cost((z - app + TILE_TOKENS - 1) / TILE_TOKENS + app);
+      }
+    } else {
+      const int app = p.step && sp.T > 0 && !sp.bad;
+      cp = lpt_half_cost((sp.T - app + TILE_TOKENS - 1) / TILE_TOKENS + app);
+    }
+  }
+
+  // Where the snake deal is already optimal, keep it (it costs less to
+  // make): every unit costs the same (equal unit counts, which the snake
+  // deal gives, are then optimal), or no workgroup gets a second unit.
+  const int cmax = wave_max(max(cf, max(cfa, cp)));
+  const int big = 1 << 30;
+  const int cmin = wave_min(min(cf > 0 ? cf : big, min(cfa > 0 ? cfa : big, cp > 0 ? cp : big)));
+  const int nunits = wave_sum(live_seq ? H * (nfa + lastapp + (cp > 0 ? 1 : 0)) : 0);
+  if (cmin == cmax || nunits <= NB) return false;
+  // Multiply-high division stays exact while every level times every cost
+  // is below 2^32: levels stay below twice the total work, so bound both.
+  const int64_t mywork = (int64_t)H * ((int64_t)nfa * cf + cfa + cp);
+  const int work = wave_sum((int)(mywork < (1 << 21) ? mywork : (1 << 21)));
+  if (cmax > (1 << 10) || work > (1 << 20)) return false;
+
+  // Loads (halved costs) of workgroups 4 lane + k; absent ones never take a slot.
+  constexpr int kAbsent = 0x3fffffff;
+  int L[4], U[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    L[k] = 4 * lane + k < NB ? 0 : kAbsent;
+    U[k] = 0;
+  }
+  int nown = 0;  // this workgroup's units so far (uniform)
+  int *own = scr + 64;  // [64][2] this workgroup's units: sequence, partition * H + head
+  for (;;) {
+    const int c = wave_max(max(cf, max(cfa, cp)));
+    if (c == 0) break;
+    const int A = cf == c ? nfa : 0, B = cfa == c ? 1 : 0, C1 = cp == c ? 1 : 0;
+    if (cf == c) cf = 0;
+    if (cfa == c) cfa = 0;
+    if (cp == c) cp = 0;
+    const int incl = wave_incl_scan_dpp(H * (A + B + C1), lane);
+    const int n = __builtin_amdgcn_readlane(incl, 63);
+    const LptDiv dc = lpt_div(c);
+
+    // Level v* of the n-th least slot: the largest v with fewer than n slots below it.
+    int lmin = kAbsent, lmax = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lmin = min(lmin, L[k]);
+      if (L[k] != kAbsent) lmax = max(lmax, L[k]);
+    }
+    lmin = wave_min(lmin);
+    lmax = wave_max(lmax);
+    auto below = [&](int v) {
+      int t = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t += lpt_slots_below(v, L[k], dc);
+      return wave_sum(t);
+    };
+    int lo = lmin, hi = lmax + ((n + NB - 1) / NB) * c;
+    while (hi - lo > 1) {
+      const int mid = lo + ((hi - lo) >> 1);
+      if (below(mid) < n)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int vstar = lo;
+    const int rest = n - below(vstar);  // slots at v* taken, lowest workgroups first
+    int ex[4], nex = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ex[k] = lpt_slot_at(vstar, L[k], dc);
+      nex += ex[k];
+    }
+    int before = wave_incl_scan_dpp(nex, lane) - nex;
+    int take[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      take[k] = lpt_slots_below(vstar, L[k], dc) + (ex[k] && before < rest ? 1 : 0);
+      before += ex[k];
+    }
+
+    // This workgroup's slots of the class, each mapped to a unit by its rank.
+    const int src = b0 >> 2, kk = b0 & 3;
+    const int myL = __builtin_amdgcn_readlane(kk == 0 ? L[0] : kk == 1 ? L[1] : kk == 2 ? L[2] : L[3], src);
+    const int myk =
+        __builtin_amdgcn_readlane(kk == 0 ? take[0] : kk == 1 ? take[1] : kk == 2 ? take[2] : take[3], src);
+    for (int i = 0; i < myk; ++i) {
+      const int v = myL + i * c;
+      int t = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int b = 4 * lane + k;
+        t += lpt_slots_below(v, L[k], dc) * 512 + ((b < b0) & lpt_slot_at(v, L[k], dc));
+      }
+      t = wave_sum(t);  // slots below v (x 512) and workgroups before this one at v
+      const int rank = (t >> 9) + (t & 511);
+      // The unit's sequence: the first whose inclusive count exceeds rank.
+      const int s = __popcll(__builtin_amdgcn_ballot_w64(incl <= rank));
+      const int r = rank - (s ? __builtin_amdgcn_readlane(incl, s - 1) : 0);
+      const int q = r / H, h = r - (r / H) * H;
+      const int As = __builtin_amdgcn_readlane(A, s), Bs = __builtin_amdgcn_readlane(B, s);
+      const int nfs = __builtin_amdgcn_readlane(sp.nfull, s);
+      const int part = q < As ? q : (q < As + Bs ? nfs - 1 : nfs);
+      if (nown < MAXU && lane == 0) {
+        own[2 * nown] = s;
+        own[2 * nown + 1] = part * H + h;
+      }
+      ++nown;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (L[k] != kAbsent) L[k] += take[k] * c;
+      U[k] += take[k];
+    }
+  }
+  if (wave_max(max(max(U[0], U[1]), max(U[2], U[3]))) > MAXU) return false;
+  lane_exchange_fence();
+
+  active = 0;
+  unit = make_int4(0, 0, 0, 0);
+  bad_part = 0;
+  const int mine_s = lane < nown ? own[2 * lane] : 0;
+  const int mine_ph = lane < nown ? own[2 * lane + 1] : 0;
+  const int T_i = __shfl(sp.T, mine_s, 64), bad_i = __shfl(sp.bad, mine_s, 64);
+  if (lane < nown) {
+    const int part = mine_ph / H, h = mine_ph - part * H;
+    int lo = 0, hi = T_i;
+    if (SPLIT) {
+      lo = part * P;
+      hi = T_i < lo + P ? T_i : lo + P;
+    }
+    const int app = p.step && T_i > 0 && hi == T_i && !bad_i;
+    active = mine_s < S && h < H && T_i >= 0;
+    if (active) {
+      unit = make_int4(mine_s, h, lo, hi - app);
+      bad_part = part * 4 + app * 2 + bad_i;
+    }
+  }
+  return true;
+}
+
 // ---- Plan cache (see DecodeParams::plan). A workgroup's slot is tagged with
 // the launch that wrote it; kind distinguishes kernels whose slots differ.
 typedef uint32_t plan_u32x4 __attribute__((ext_vector_type(4)));
@@ -262,7 +535,7 @@ __device__ inline PlanSlot plan_slot(const DecodeParams &p, uint32_t kind, int w
 // here and, with a buffer, stored with the tag for the launches after this
 // one. Every path issues the same stores (the unwanted ones go past
 // num_records and are dropped).
-template <bool SPLIT>
+template <bool SPLIT, int TILE_TOKENS>
 __device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot &ps, int lane,
                                           int *scr, int4 &my, int &my_bp, int &my_act) {
   if (ps.use) {
@@ -275,7 +548,10 @@ __device__ inline void plan_or_load_units(const DecodeParams &p, const PlanSlot 
              (bp >> 2) < (SPLIT ? p.max_parts : 1) && (p.step || (bp & 2) == 0);
     my_bp = my_act ? bp : 0;
     if (!my_act) my = make_int4(0, 0, 0, 0);
-  } else {
+  } else if (!p.plan || !plan_units_lpt<SPLIT, TILE_TOKENS>(p, lane, scr, my, my_bp, my_act)) {
+    // Without a plan buffer every launch deals for itself, and there the
+    // snake deal pays: on the mixed batch the longest-first deal takes about
+    // 12 us longer to make than it saves in one launch (2.7 us).
     plan_units<SPLIT>(p, lane, scr, my, my_bp, my_act);
   }
   if (p.plan) {

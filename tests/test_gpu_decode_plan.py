@@ -239,3 +239,47 @@ def test_plan_buffer_across_random_batches():
             for e in (epoch, epoch, epoch | 0x80000000):
                 for a, b in zip(want, _partitioned(t, case, P, plan, e)):
                     assert np.array_equal(a, b), (k, e)
+
+
+@pytest.mark.parametrize("k", range(10))
+def test_longest_first_deal_random_batches(k):
+    """Batches of at most 64 sequences with partitions of several sizes (the
+    launches that store a plan deal them longest-first): the planning call
+    and a call that reads the stored plan give the unplanned bits, as a step
+    and as a plain partitioned call, and the step matches the oracle."""
+    rng = np.random.default_rng(500 + k)
+    S = int(rng.integers(2, 65))
+    lens = [int(x) for x in np.exp(rng.uniform(np.log(16), np.log(9000), S))]
+    P = int(rng.choice([256, 512, 1024, 1792, 2048]))
+    print(f"[plan] longest-first batch {k}: S={S} P={P}", flush=True)
+    case = inputs.decode_case(lens, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2, seed=700 + k)
+    plan = pa.decode_plan_buffer()
+    base, _ = _step(case, P)
+    for e in (31 + k, 31 + k):
+        got, _ = _step(case, P, plan, e)
+        assert np.array_equal(G.bits(base), G.bits(got)), e
+    assert G.max_err(G.host(got), _oracle_step(case)) <= G.BF16_TOL
+    t = G.to_dev(case)
+    G.write(t)
+    want = _partitioned(t, case, P)
+    for e in (900 + k, 900 + k):
+        for a, b in zip(want, _partitioned(t, case, P, plan, e)):
+            assert np.array_equal(a, b), e
+
+
+def test_longest_first_deal_fp8():
+    """The FP8 kernel's longest-first deal (mixed batch, its 2048-token
+    partitions and a 1024-token one): planning and reading calls give the
+    unplanned bits."""
+    from tests.test_gpu_fp8 import _fp8_case, _write
+    import bench
+    ks, vs = bench.FP8_SCALES["mixed"]
+    case = inputs.preset_case("mixed", seed=3)
+    t, _, _ = _fp8_case(case, ks, vs)
+    _write(t, ks, vs)
+    for P in (G.bench_partitions()[1]["mixed"], 1024):
+        want = _fp8_records(t, case, P, ks, vs)
+        plan = pa.decode_plan_buffer()
+        for _ in range(2):
+            for a, b in zip(want, _fp8_records(t, case, P, ks, vs, plan, 77)):
+                assert np.array_equal(a, b), P
