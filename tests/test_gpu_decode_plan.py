@@ -251,8 +251,9 @@ def test_longest_first_deal_random_batches(k):
     S = int(rng.integers(2, 65))
     lens = [int(x) for x in np.exp(rng.uniform(np.log(16), np.log(9000), S))]
     P = int(rng.choice([256, 512, 1024, 1792, 2048]))
-    print(f"[plan] longest-first batch {k}: S={S} P={P}", flush=True)
-    case = inputs.decode_case(lens, 24, 4, 256, 16, dtype="bf16", pool_factor=1.2, seed=700 + k)
+    hq, hkv = [(24, 4), (16, 8), (8, 1), (24, 3)][k % 4]
+    print(f"[plan] longest-first batch {k}: S={S} P={P} heads {hq}/{hkv}", flush=True)
+    case = inputs.decode_case(lens, hq, hkv, 256, 16, dtype="bf16", pool_factor=1.2, seed=700 + k)
     plan = pa.decode_plan_buffer()
     base, _ = _step(case, P)
     for e in (31 + k, 31 + k):
