@@ -366,7 +366,9 @@ __device__ inline bool plan_units_lpt(const DecodeParams &p, int lane, int *scr,
     L[k] = 4 * lane + k < NB ? 0 : kAbsent;
     U[k] = 0;
   }
-  int nown = 0;  // this workgroup's units so far (uniform)
+  int nown = 0;         // this workgroup's units so far (uniform)
+  int floor_level = 0;  // every load is at least this
+  int lmax = 0;         // no load is above this
   int *own = scr + 64;  // [64][2] this workgroup's units: sequence, partition * H + head
   for (;;) {
     const int c = wave_max(max(cf, max(cfa, cp)));
@@ -379,38 +381,39 @@ __device__ inline bool plan_units_lpt(const DecodeParams &p, int lane, int *scr,
     const int n = __builtin_amdgcn_readlane(incl, 63);
     const LptDiv dc = lpt_div(c);
 
-    // Level v* of the n-th least slot: the largest v with fewer than n slots below it.
-    int lmin = kAbsent, lmax = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lmin = min(lmin, L[k]);
-      if (L[k] != kAbsent) lmax = max(lmax, L[k]);
-    }
-    lmin = wave_min(lmin);
-    lmax = wave_max(lmax);
+    // Level v* of the n-th least slot: the largest v with fewer than n slots
+    // below it. After a class every load is at least that class's level
+    // (the workgroups below it took every slot up to it), so the search
+    // starts there with no slot below; the highest load is at most the
+    // previous highest or the last level plus its cost.
     auto below = [&](int v) {
       int t = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) t += lpt_slots_below(v, L[k], dc);
       return wave_sum(t);
     };
-    int lo = lmin, hi = lmax + ((n + NB - 1) / NB) * c;
+    int lo = floor_level, hi = lmax + ((n + NB - 1) / NB) * c, below_lo = 0;
     while (hi - lo > 1) {
       const int mid = lo + ((hi - lo) >> 1);
-      if (below(mid) < n)
+      const int bm = below(mid);
+      if (bm < n) {
         lo = mid;
-      else
+        below_lo = bm;
+      } else {
         hi = mid;
+      }
     }
     const int vstar = lo;
-    const int rest = n - below(vstar);  // slots at v* taken, lowest workgroups first
-    int ex[4], nex = 0;
+    const int rest = n - below_lo;  // slots at v* taken, lowest workgroups first
+    // Workgroups with a slot at v* in lower-indexed lanes: one ballot per
+    // workgroup of a lane, counted below this lane with mbcnt.
+    int ex[4], before = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       ex[k] = lpt_slot_at(vstar, L[k], dc);
-      nex += ex[k];
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ex[k] != 0);
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
     }
-    int before = wave_incl_scan_dpp(nex, lane) - nex;
     int take[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -451,6 +454,8 @@ __device__ inline bool plan_units_lpt(const DecodeParams &p, int lane, int *scr,
       if (L[k] != kAbsent) L[k] += take[k] * c;
       U[k] += take[k];
     }
+    floor_level = vstar;
+    lmax = max(lmax, vstar + c);
   }
   if (wave_max(max(max(U[0], U[1]), max(U[2], U[3]))) > MAXU) return false;
   lane_exchange_fence();
