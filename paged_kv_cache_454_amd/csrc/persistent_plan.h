@@ -213,7 +213,7 @@ __device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int
 // one. plan_units_lpt deals the same units longest-first instead: each unit,
 // largest first, goes to the workgroup with the least work so far (ties to
 // the lowest index). A unit's cost is the stream positions it gives wave 0
-// (the most of any wave): ceil(tiles / NWAVES), padded to even. The result
+// (the most of any wave): ceil(tiles / kPlanWaves), padded to even. The result
 // does not depend on the deal (a unit's arithmetic is the same on every
 // workgroup); only the balance does. It is made by launches that store
 // their plan (a step's later layers read it) and only where it can beat
@@ -222,8 +222,9 @@ __device__ inline void plan_units(const DecodeParams &p, int lane, int *scr, int
 // Units of equal cost are dealt at once: with costs c, the greedy choice is
 // the least (load + i c, workgroup) "slot" among all workgroups' free slots,
 // so n units of cost c take the n least slots in that order. A binary search
-// on the slot value finds the level of the n-th slot, and the workgroups
-// just below it, lowest index first, take the rest. Within a cost class the
+// on the slot value finds the level of the n-th slot: every slot below it is
+// taken, and of the slots at it, those of the lowest-indexed workgroups
+// make up the rest. Within a cost class the
 // units are numbered by sequence, then partition, then head, and a
 // workgroup's slots map to those numbers by their rank among all slots.
 constexpr int kPlanWaves = 8;       // wavefronts of the persistent kernels
