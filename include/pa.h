@@ -327,6 +327,13 @@ pa_status pa_decode_step(void *out, float *part_out, float *part_max, float *par
  * Launches that share a buffer must run in order (one stream). Where the
  * matrix-core kernel does not take the shape the buffer is not used. Results
  * are bit for bit those of the calls without a plan.
+ *
+ * A launch that plans and stores its slots deals the units longest-first by
+ * work (each, largest first, to the workgroup with the least work so far)
+ * where that can beat the plain deal of launches without a buffer, for
+ * batches of up to 64 sequences. That deal takes longer to make (about 11 us
+ * against 2 us on a 64-sequence batch with 420 units) and is repaid by the
+ * launches that read it: pass a buffer when later layers will read the plan.
  */
 size_t pa_decode_plan_bytes(void);
 
