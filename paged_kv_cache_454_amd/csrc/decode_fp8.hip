@@ -398,20 +398,21 @@ void decode_fp8_kernel(DecodeParams p) {
   // S^T, softmax and the weights (B operand of P.V) for one tile.
   auto qk_softmax = [&](const u32x4(&kraw)[KL], int qslot, int nvalid) -> u32x4 {
     // Loads 2p, 2p+1 of a half give lane m < 8 row m's piece j = 2p and lane
-    // m >= 8 row m's piece j = 2p+1; each lane passes the piece its partner
-    // m ^ 8 needs (row rotation by 8) and keeps its own.
+    // m >= 8 row m's piece j = 2p+1; each lane takes the piece it lacks from
+    // its partner m ^ 8 (row rotation by 8) and keeps its own. The rotation
+    // writes only the receiving half of each 16-lane row (DPP bank mask:
+    // lanes 8-15 = banks 2, 3; lanes 0-7 = banks 0, 1), so the other half
+    // keeps the old value, its own piece, and no selects are needed.
     u32x4 kt[KL];
-    const bool lo8 = n16 < 8;
 #pragma unroll
     for (int hp = 0; hp < 4; ++hp) {
       const u32x4 v0 = kraw[2 * hp], v1 = kraw[2 * hp + 1];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t send = lo8 ? v1[w] : v0[w];
-        const uint32_t recv =
-            (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x128, 0xf, 0xf, false);
-        kt[2 * hp][w] = lo8 ? v0[w] : recv;
-        kt[2 * hp + 1][w] = lo8 ? recv : v1[w];
+        kt[2 * hp][w] =
+            (uint32_t)__builtin_amdgcn_update_dpp((int)v0[w], (int)v1[w], 0x128, 0xf, 0xc, false);
+        kt[2 * hp + 1][w] =
+            (uint32_t)__builtin_amdgcn_update_dpp((int)v1[w], (int)v0[w], 0x128, 0xf, 0x3, false);
       }
     }
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
