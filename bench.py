@@ -72,6 +72,11 @@ PREFILL_TRAFFIC_SOURCES = [os.path.join(_CSRC, f) for f in ("prefill_mfma.hip", 
 # are left to balance the CUs). The FP8 leg: 1.005 ms at 512, 0.928 ms at
 # 1024, 0.931 ms at 1792, 0.915 ms at 2048; on the long-context batch its
 # decode takes 44.5 us at 512, 38.1 us at 1536 and 39.7-39.9 us at 2048.
+# Bit 31 of a plan epoch: the launch plans afresh and stores its slots under
+# the epoch without the bit. A step's first layer sets it, so that launch plans
+# whatever an earlier user of the buffer's memory left there; the later layers
+# read its slots.
+PLAN_REFRESH = 0x80000000
 DEFAULT_PARTITION = {"mixed": 1792, "long": 512, "uniform": 256}
 FP8_DEFAULT_PARTITION = {"mixed": 2048, "long": 1536, "uniform": 256}
 WORKLOAD_NAMES = {
@@ -119,7 +124,10 @@ def parse():
                          "counter runs that should see one form's launches)")
     ap.add_argument("--side-decode", type=int, default=1,
                     help="with the mixed workload, also time the long-context and uniform "
-                         "decode workloads (0: skip)")
+                         "decode workloads, each in a process of its own (0: skip)")
+    ap.add_argument("--leg-json", type=int, default=0,
+                    help="print only this workload's decode leg as one JSON line (how the "
+                         "mixed run times its long-context and uniform legs)")
     ap.add_argument("--loop-steps", type=int, default=50,
                     help="timed iterations of the continuous-batching loop leg (0 skips it)")
     ap.add_argument("--prefill-reps", type=int, default=10,
@@ -263,8 +271,13 @@ def prefill_leg(seed, reps, dev):
                             t["block_tables"], t["query_start_loc"], t["context_lens"],
                             m["max_query_len"], m["scale"], stream=stream)
 
+    # Untimed launches first: the matrix cores' clock ramps over the first
+    # tens of ms of this load (measured: one warm-up launch, then 10 timed
+    # ones averaged 770-790 us; the next 10 took 702-706 us, the 10 after
+    # those 679-687 us).
     write()
-    prefill()
+    for _ in range(max(20, 3 * reps)):
+        prefill()
     torch.cuda.synchronize()
     w_ms = timed_launches(write, reps, stream)
     p_ms = timed_launches(prefill, reps, stream)
@@ -566,7 +579,8 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
         if li == 0:
             epoch[0] += 1
         pa.pa_decode_partitioned_fp8(po, pm, ps, layers[li]["query"], kc, vc, bt, cl, scale, ks,
-                                     vs, P, stream=stream, plan=plan, plan_epoch=epoch[0])
+                                     vs, P, stream=stream, plan=plan,
+                                     plan_epoch=epoch[0] | (PLAN_REFRESH if li == 0 else 0))
 
     def step():
         for li, L in enumerate(layers):
@@ -663,7 +677,8 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
     # Plan buffers: the layers (pool sets) of a step share context lengths
     # and block tables, so the first launch of a step plans and the others
     # read its plan. Each step takes a new epoch (the lengths and tables of a
-    # real step change every step), so every step plans once. plan_step
+    # real step change every step), so every step plans once, in its first
+    # layer's launch (refresh bit set). plan_step
     # serves the fused step, plan_dec the planned partitioned decode.
     plan_step = pa.decode_plan_buffer(dev)
     plan_dec = pa.decode_plan_buffer(dev)
@@ -686,7 +701,8 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
         else:
             pa.pa_decode_partitioned_planned(po, pm, ps, L["query"], L["key_cache"],
                                              L["value_cache"], bt, cl, scale, P, plan_dec,
-                                             epoch[0], stream=stream)
+                                             epoch[0] | (PLAN_REFRESH if li == 0 else 0),
+                                             stream=stream)
 
     def step_calls():
         for li, L in enumerate(layers):
@@ -703,7 +719,8 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
             pa.pa_decode_step(outs[li], L["query"], L["key"], L["value"], L["key_cache"],
                               L["value_cache"], bt, cl, scale, P if split else 0,
                               po if split else None, pm if split else None,
-                              ps if split else None, plan=plan_step, plan_epoch=epoch[0],
+                              ps if split else None, plan=plan_step,
+                              plan_epoch=epoch[0] | (PLAN_REFRESH if li == 0 else 0),
                               stream=stream)
 
     def time_steps(step):
@@ -777,12 +794,40 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
     return res
 
 
+def side_leg(w2, args):
+    """One of the other two decode workloads, timed by a child bench.py of its
+    own. Pools that a process allocates after earlier allocations went back
+    to the driver gather more slowly: the long-context leg took 63.8-64.6 us
+    as a second leg of one process (or after a 10 GiB allocate / free
+    cycle) against 61.4-61.9 us as the first, same kernel and data. A serving
+    process allocates its cache once at start-up, so each workload is timed
+    on the memory a fresh process gets. The children run before this process
+    touches the GPU."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", w2,
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--seed", str(args.seed),
+           "--fp8", str(args.fp8 if w2 == "long" else 0),
+           "--compare-step", str(args.compare_step), "--leg-json", "1", "--side-decode", "0",
+           "--prefill-reps", "0", "--loop-steps", "0", "--cpu-seconds", "0"]
+    if args.step:
+        cmd += ["--step", args.step]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr[-4000:])
+        raise RuntimeError(f"bench.py: the {w2} decode leg failed (exit {r.returncode})")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is not implemented", file=sys.stderr)
         sys.exit(2)
+    side = {}
+    if args.side_decode and args.workload == "mixed" and not args.leg_json:
+        for w2 in ("long", "uniform"):
+            side[w2] = side_leg(w2, args)
     import torch
 
     dev = torch.device("cuda:0")
@@ -793,6 +838,9 @@ def main():
     mode = args.mode or DEFAULT_MODE[W]
     main_leg = decode_leg(W, P, args.steps, args.warmup, dev, args.seed, fp8_P, mode,
                           args.step or DEFAULT_STEP[W], bool(args.compare_step))
+    if args.leg_json:
+        print(json.dumps(main_leg), flush=True)
+        return
 
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) + tokens/s, 1 GPU",
@@ -818,13 +866,9 @@ def main():
         result["fp8"] = main_leg["fp8"]
     # The other two decode configurations of the target (long-context split
     # decode at its stated 512-token partitions; uniform batch), each with its
-    # own step time and kernel roofline; they do not enter `value`.
-    if args.side_decode and W == "mixed":
-        for w2 in ("long", "uniform"):
-            f2 = FP8_DEFAULT_PARTITION[w2] if (args.fp8 and w2 == "long") else None
-            result[w2] = decode_leg(w2, DEFAULT_PARTITION[w2], args.steps, args.warmup, dev,
-                                    args.seed, f2, DEFAULT_MODE[w2],
-                                    args.step or DEFAULT_STEP[w2], bool(args.compare_step))
+    # own step time and kernel roofline, timed first in processes of their own
+    # (side_leg); they do not enter `value`.
+    result.update(side)
     if args.prefill_reps > 0:
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.seed, args.prefill_reps, dev)
