@@ -86,7 +86,7 @@ WORKLOAD_NAMES = {
 }
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -133,7 +133,7 @@ def parse():
     ap.add_argument("--prefill-reps", type=int, default=10,
                     help="timed repetitions of the side legs, chunked prefill and "
                          "copy-on-write block copies (0 skips them)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def cpu_baseline(seed, budget_s, single_core_s=6.0):

@@ -227,3 +227,49 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bench_side_legs_run_in_child_processes(monkeypatch):
+    """The mixed run times the long-context and uniform legs by child
+    bench.py processes (each on the memory a fresh process gets): each child
+    gets its workload, the step settings, FP8 only for the long-context leg
+    and no nested side legs; its last stdout line is the leg's JSON; a failed
+    child raises. The children start before the parent touches a GPU."""
+    import json
+    import subprocess
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    calls = []
+
+    def fake_run(cmd, capture_output, text, timeout):
+        calls.append(cmd)
+        w = cmd[cmd.index("--workload") + 1]
+        return subprocess.CompletedProcess(cmd, 0, stdout="noise\n" + json.dumps({"leg": w}) + "\n",
+                                           stderr="")
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    args = bench.parse(["--steps", "7", "--warmup", "2", "--step", "calls"])
+    for w2 in ("long", "uniform"):
+        assert bench.side_leg(w2, args) == {"leg": w2}
+    (c_long, c_uni) = calls
+    opt = lambda c, k: c[c.index(k) + 1]
+    for c, w in ((c_long, "long"), (c_uni, "uniform")):
+        assert c[0] == sys.executable and c[1].endswith("bench.py")
+        assert opt(c, "--workload") == w and opt(c, "--leg-json") == "1"
+        assert opt(c, "--side-decode") == "0" and opt(c, "--prefill-reps") == "0"
+        assert opt(c, "--steps") == "7" and opt(c, "--warmup") == "2"
+        assert opt(c, "--step") == "calls"
+        assert "--partition-size" not in c and "--mode" not in c
+    assert opt(c_long, "--fp8") == "1" and opt(c_uni, "--fp8") == "0"
+
+    def failing_run(cmd, capture_output, text, timeout):
+        return subprocess.CompletedProcess(cmd, 3, stdout="", stderr="boom")
+
+    monkeypatch.setattr(subprocess, "run", failing_run)
+    with pytest.raises(RuntimeError, match="long decode leg failed"):
+        bench.side_leg("long", args)
+    # The side legs are started in main() before torch is imported there.
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    body = src[src.index("\ndef main():"):]
+    assert body.index("side_leg(w2, args)") < body.index("import torch")
