@@ -571,7 +571,8 @@ def fp8_leg(layers, meta, P, steps, warmup, dev, workload, seed):
     scale = meta["scale"]
     stream = torch.cuda.current_stream()
 
-    plan = pa.decode_plan_buffer(dev)
+    # One-layer workloads: every launch plans for itself (see decode_leg).
+    plan = None if "layers" not in inputs.PRESETS[workload] else pa.decode_plan_buffer(dev)
     epoch = [0]
 
     def decode(li):
@@ -674,14 +675,17 @@ def decode_leg(W, P, steps, warmup, dev, seed, fp8_P=None, mode="split", step_fo
     stream = torch.cuda.current_stream()
 
     scratch = pa.decode_scratch(dev)
-    # Plan buffers: the layers (pool sets) of a step share context lengths
-    # and block tables, so the first launch of a step plans and the others
-    # read its plan. Each step takes a new epoch (the lengths and tables of a
-    # real step change every step), so every step plans once, in its first
-    # layer's launch (refresh bit set). plan_step
-    # serves the fused step, plan_dec the planned partitioned decode.
-    plan_step = pa.decode_plan_buffer(dev)
-    plan_dec = pa.decode_plan_buffer(dev)
+    # Plan buffers: the layers of a step share context lengths and block
+    # tables, so the first launch of a step plans and the others read its
+    # plan. Each step takes a new epoch (the lengths and tables of a real step
+    # change every step), so every step plans once, in its first layer's
+    # launch (refresh bit set). plan_step serves the fused step, plan_dec the
+    # planned partitioned decode. The pool sets of a one-layer workload are
+    # successive steps of that layer, not layers of one step: there every
+    # launch plans for itself (no buffer).
+    one_layer = "layers" not in pre
+    plan_step = None if one_layer else pa.decode_plan_buffer(dev)
+    plan_dec = None if one_layer else pa.decode_plan_buffer(dev)
     epoch = [0]
 
     def decode(li):
